@@ -1,0 +1,433 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Every check here uses a value fixed by the pages or by mathematics:
+high-precision brute force on tiny inputs, closed forms (two keys, zero
+keys under each mask, a single dominant key), invariants (mass conservation,
+GQA = repeated MHA, permutation equivariance, the supplied-LSE identity),
+library routines for the special cases they cover, brute-force rank
+counting for the budget, the token counts printed in the LiteVLM review's
+main-results table for the budget rule, and a token-by-token loop for the
+compaction.  The last group plants mistakes in a copy of the oracle's
+arithmetic and checks that the pins catch them.
+"""
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import tsel_oracle as O
+from workloads import Problem, layout_arrays, make_config, make_problem, random_small
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def handmade(requests, q, k, mask, ratios=1.0, emb_dim=4):
+    """Problem from explicit fp64-representable Q/K values (stored as fp32)."""
+    cu, cui, st, hw, cc = layout_arrays(requests)
+    T = int(cu[-1])
+    q = torch.as_tensor(np.asarray(q, np.float32))
+    k = torch.as_tensor(np.asarray(k, np.float32))
+    assert q.shape[0] == T and k.shape[0] == T
+    B = len(cu) - 1
+    return Problem(name="hand", q=q, k=k, mask=mask, cu_seqlens=cu, cu_images=cui,
+                   img_start=st, img_hw=hw, cu_cands=cc,
+                   keep_ratio=np.broadcast_to(np.float64(ratios), (B,)).copy(),
+                   emb=torch.arange(T * emb_dim, dtype=torch.float32).reshape(T, emb_dim),
+                   dtype="f32")
+
+
+def visible(prob, i, j):
+    """Visibility straight from the mask's wording, token by token."""
+    cu = prob.cu_seqlens
+    bi = np.searchsorted(cu, i, side="right") - 1
+    bj = np.searchsorted(cu, j, side="right") - 1
+    if bi != bj:
+        return False
+    if prob.mask == "causal":
+        return j <= i
+    if prob.mask == "blockdiag":
+        def img(t):
+            for s in range(prob.S):
+                n = prob.img_hw[s, 0] * prob.img_hw[s, 1]
+                if prob.img_start[s] <= t < prob.img_start[s] + n:
+                    return s
+            return -1
+        return img(i) == img(j) and img(i) >= 0
+    return True
+
+
+def mp_reference(prob):
+    """50-digit brute force: LSE per (h, i) and mass per candidate."""
+    mpmath.mp.dps = 50
+    q = O.to_f64(prob.q)
+    k = O.to_f64(prob.k)
+    T, hq, d = q.shape
+    rep = hq // k.shape[1]
+    scale = 1 / mpmath.sqrt(d)
+    cand_tok = []
+    for s in range(prob.S):
+        n = int(prob.img_hw[s, 0] * prob.img_hw[s, 1])
+        cand_tok += list(range(int(prob.img_start[s]), int(prob.img_start[s]) + n))
+    lse = [[None] * T for _ in range(hq)]
+    mass = [mpmath.mpf(0)] * len(cand_tok)
+    for h in range(hq):
+        g = h // rep
+        for i in range(T):
+            logits = {}
+            for j in range(T):
+                if visible(prob, i, j):
+                    logits[j] = scale * mpmath.fsum(mpmath.mpf(float(q[i, h, t])) *
+                                                    mpmath.mpf(float(k[j, g, t])) for t in range(d))
+            if not logits:
+                continue
+            L = mpmath.log(mpmath.fsum(mpmath.exp(v) for v in logits.values()))
+            lse[h][i] = L
+            for c, j in enumerate(cand_tok):
+                if j in logits:
+                    mass[c] += mpmath.exp(logits[j] - L)
+    return lse, mass
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "blockdiag"])
+def test_mpmath_bruteforce_tiny(mask):
+    rng = np.random.default_rng(11)
+    if mask == "blockdiag":
+        reqs = [(7, [(0, 1, 3), (3, 2, 2)])]
+    else:
+        reqs = [(5, [(1, 1, 3)]), (3, [(0, 1, 2)])]
+    T = sum(r[0] for r in reqs)
+    q = rng.standard_normal((T, 2, 4)) * 1.5
+    k = rng.standard_normal((T, 1, 4)) * 1.5
+    prob = handmade(reqs, q, k, mask)
+    lse, mass = oracle.attention_stats(prob)
+    ref_lse, ref_mass = mp_reference(prob)
+    for h in range(2):
+        for i in range(T):
+            if ref_lse[h][i] is not None:
+                assert abs(lse[h, i] - float(ref_lse[h][i])) <= 1e-12 * max(1, abs(lse[h, i]))
+    for c in range(prob.N):
+        assert abs(mass[c] - float(ref_mass[c])) <= 1e-12 * max(1.0, float(ref_mass[c]))
+
+
+def test_two_keys_logistic_closed_form():
+    """Full mask, two tokens: P(i -> key 0) = sigmoid(s_i0 - s_i1)."""
+    rng = np.random.default_rng(3)
+    d = 8
+    q = rng.standard_normal((2, 3, d))
+    k = rng.standard_normal((2, 3, d))
+    prob = handmade([(2, [(0, 1, 2)])], q, k, "full")
+    q64, k64 = O.to_f64(prob.q), O.to_f64(prob.k)
+    _, mass = oracle.attention_stats(prob)
+    want = np.zeros(2)
+    for h in range(3):
+        for i in range(2):
+            s0 = q64[i, h] @ k64[0, h] / math.sqrt(d)
+            s1 = q64[i, h] @ k64[1, h] / math.sqrt(d)
+            p0 = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+            want += [p0, 1.0 - p0]
+    np.testing.assert_allclose(mass, want, rtol=1e-13)
+
+
+def harmonic(m):
+    return sum(1.0 / i for i in range(1, m + 1))
+
+
+def test_zero_keys_full_is_uniform():
+    n, hq = 37, 3
+    q = np.random.default_rng(0).standard_normal((n, hq, 16))
+    prob = handmade([(n, [(0, 1, n)])], q, np.zeros((n, 1, 16)), "full")
+    _, mass = oracle.attention_stats(prob)
+    np.testing.assert_allclose(mass, hq, rtol=1e-13)
+    np.testing.assert_allclose(oracle.scores(prob, mass), 1.0 / n, rtol=1e-13)
+
+
+def test_zero_keys_causal_harmonic():
+    """Row i sees i+1 keys uniformly: mass_j = Hq * (H_n - H_j), j 0-based."""
+    n, hq = 41, 2
+    q = np.random.default_rng(1).standard_normal((n, hq, 16))
+    prob = handmade([(n, [(0, 1, n)])], q, np.zeros((n, 2, 16)), "causal")
+    _, mass = oracle.attention_stats(prob)
+    want = [hq * (harmonic(n) - harmonic(j)) for j in range(n)]
+    np.testing.assert_allclose(mass, want, rtol=1e-13)
+
+
+def test_zero_keys_causal_text_prefix_scale_zero():
+    """scale = 0 is the same as zero keys; with a text prefix of p tokens the
+    candidate at token t gets Hq * (H_n - H_t)."""
+    n, p, hq = 30, 7, 2
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((n, hq, 8))
+    k = rng.standard_normal((n, 1, 8))
+    prob = handmade([(n, [(p, 2, 9)])], q, k, "causal")
+    _, mass = oracle.attention_stats(prob, scale=0.0)
+    want = [hq * (harmonic(n) - harmonic(t)) for t in range(p, p + 18)]
+    np.testing.assert_allclose(mass, want, rtol=1e-13)
+
+
+def test_zero_keys_blockdiag_unequal_images():
+    sizes = [(2, 3), (5, 7), (1, 4)]
+    imgs, off = [], 0
+    for h, w in sizes:
+        imgs.append((off, h, w))
+        off += h * w
+    hq = 4
+    q = np.random.default_rng(4).standard_normal((off, hq, 8))
+    prob = handmade([(off, imgs)], q, np.zeros((off, 4, 8)), "blockdiag")
+    _, mass = oracle.attention_stats(prob)
+    np.testing.assert_allclose(mass, hq, rtol=1e-13)
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "blockdiag"])
+def test_mass_conservation_all_candidates(mask):
+    """Every token a candidate and the LSE computed: sum_c mass = Hq * n_b."""
+    rng = np.random.default_rng(5)
+    if mask == "blockdiag":
+        reqs = [(60, [(0, 5, 6), (30, 3, 10)])]
+    else:
+        reqs = [(48, [(0, 6, 8)]), (35, [(0, 5, 7)])]
+    T = sum(r[0] for r in reqs)
+    prob = handmade(reqs, rng.standard_normal((T, 4, 16)) * 2,
+                    rng.standard_normal((T, 2, 16)) * 2, mask)
+    _, mass = oracle.attention_stats(prob)
+    for b, (lo, hi) in enumerate(oracle.pool_bounds(prob)):
+        n_b = prob.cu_seqlens[b + 1] - prob.cu_seqlens[b]
+        assert abs(mass[lo:hi].sum() - 4 * n_b) <= 1e-11 * n_b
+    sc = oracle.scores(prob, mass)
+    for lo, hi in oracle.pool_bounds(prob):
+        assert abs(sc[lo:hi].sum() - 1.0) < 1e-12
+
+
+def test_single_dominant_key():
+    """k* = alpha * u with q_i . u > 0 for all rows: it is the top-1 key, each
+    row's probability obeys 1/(1 + (n-1) e^{-delta_i}) <= P, and for a large
+    alpha the mass tends to Hq * (rows that see k*)."""
+    rng = np.random.default_rng(6)
+    n, hq, d, j = 50, 2, 16, 20
+    u = np.zeros(d)
+    u[0] = 1.0
+    q = rng.standard_normal((n, hq, d)) * 0.3
+    q[:, :, 0] = np.abs(q[:, :, 0]) + 1.0
+    k = rng.standard_normal((n, 1, d)) * 0.3
+    for alpha, check_limit in ((20.0, False), (4000.0, True)):
+        kk = k.copy()
+        kk[j, 0] = alpha * u
+        prob = handmade([(n, [(0, 5, 10)])], q, kk, "causal")
+        lse, mass = oracle.attention_stats(prob)
+        sc = oracle.scores(prob, mass)
+        assert int(np.argmax(sc)) == j
+        q64, k64 = O.to_f64(prob.q), O.to_f64(prob.k)
+        for h in range(hq):
+            for i in range(j, n):
+                s = q64[i, h] @ k64[: i + 1, 0].T / math.sqrt(d)
+                delta = s[j] - np.max(np.delete(s, j))
+                p = math.exp(s[j] - lse[h, i])
+                assert p >= 1.0 / (1.0 + i * math.exp(-delta)) - 1e-12
+        if check_limit:
+            assert abs(mass[j] - hq * (n - j)) < 1e-9
+
+
+def test_gqa_equals_repeated_mha():
+    p = make_problem("g", [(90, [(10, 5, 12)])], 8, 2, 32, "f32", "causal", 1.0, 7, ratios=0.5)
+    _, mass_g = oracle.attention_stats(p)
+    k_rep = p.k.repeat_interleave(4, dim=1)
+    p2 = make_problem("m", [(90, [(10, 5, 12)])], 8, 8, 32, "f32", "causal", 1.0, 7, ratios=0.5)
+    p2.q, p2.k = p.q, k_rep
+    _, mass_m = oracle.attention_stats(p2)
+    np.testing.assert_allclose(mass_g, mass_m, rtol=1e-12)
+
+
+def test_permutation_equivariance_full_mask():
+    p = make_problem("p", [(64, [(0, 8, 8)])], 3, 3, 16, "f32", "full", 1.0, 8, ratios=0.5)
+    _, mass = oracle.attention_stats(p)
+    perm = np.random.default_rng(9).permutation(64)
+    p.q, p.k = p.q[perm], p.k[perm]
+    _, mass_p = oracle.attention_stats(p)
+    np.testing.assert_allclose(mass_p, mass[perm], rtol=1e-12)
+
+
+def test_supplied_lse_identity_and_shift():
+    """Supplied LSE equal to the computed one gives the same mass; LSE + delta
+    scales every mass by exp(-delta)."""
+    p = random_small(12, "causal", dtype="f32")
+    lse, mass = oracle.attention_stats(p)
+    _, mass_same = oracle.attention_stats(p, lse_in=lse)
+    np.testing.assert_array_equal(mass_same, mass)
+    delta = 0.37
+    _, mass_shift = oracle.attention_stats(p, lse_in=lse + delta)
+    np.testing.assert_allclose(mass_shift, mass * math.exp(-delta), rtol=1e-13)
+
+
+def test_lse_and_softmax_match_library_routines():
+    """Full mask, one request: the LSE is scipy's logsumexp of the logits and
+    the mass is the column sum of torch's float64 softmax."""
+    p = make_problem("l", [(70, [(0, 7, 10)])], 2, 2, 24, "f32", "full", 1.5, 10, ratios=0.5)
+    lse, mass = oracle.attention_stats(p)
+    q64 = torch.from_numpy(O.to_f64(p.q))
+    k64 = torch.from_numpy(O.to_f64(p.k))
+    want_mass = np.zeros(70)
+    for h in range(2):
+        logits = (q64[:, h] @ k64[:, h].T / math.sqrt(24)).numpy()
+        np.testing.assert_allclose(lse[h], scipy.special.logsumexp(logits, axis=1), rtol=1e-13)
+        want_mass += torch.softmax(torch.from_numpy(logits), dim=1).sum(0).numpy()
+    np.testing.assert_allclose(mass, want_mass, rtol=1e-12)
+
+
+def test_named_workloads_shapes():
+    """Sizes of the five workloads (cheap: no scoring)."""
+    p1 = make_config(1)
+    assert (p1.T, p1.hq, p1.d, p1.N, len(p1.dominant)) == (256, 4, 64, 256, 8)
+    p3 = make_config(3)
+    assert (p3.T, p3.S, p3.N, p3.d) == (30720, 30, 30720, 80)
+    assert 15 * 10 <= len(p3.dominant) <= 15 * 20
+    p4 = make_config(4)
+    assert (p4.T, p4.hq, p4.hkv, p4.N) == (16384, 64, 8, 15000)
+    p5 = make_config(5)
+    assert p5.B == 8 and all(2048 <= n <= 8192 for n in np.diff(p5.cu_seqlens))
+    for b in range(8):
+        lo, hi = oracle.pool_bounds(p5)[b]
+        assert hi - lo <= p5.cu_seqlens[b + 1] - p5.cu_seqlens[b] - 1
+        assert 0.5 <= p5.keep_ratio[b] < 0.9
+
+
+# ---------------------------------------------------------------------------
+# Budget and top-k.
+# ---------------------------------------------------------------------------
+
+def read_golden_counts():
+    rows = []
+    with open(os.path.join(GOLDEN, "p1_token_counts.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, vis, text, r, printed = line.split()
+                rows.append((name, int(vis), int(text), float(r), int(printed)))
+    return rows
+
+
+def test_budget_rule_reproduces_litevlm_table():
+    rows = read_golden_counts()
+    assert len(rows) == 5
+    for name, vis, text, r, printed in rows:
+        assert oracle.budget_k(r, vis) + text == printed, name
+
+
+def test_budget_rule_named_workloads_and_edges():
+    assert oracle.budget_k(0.4, 256) == 102
+    assert oracle.budget_k(0.8, 3072) == 2457
+    assert oracle.budget_k(0.6, 30720) == 18432
+    assert oracle.budget_k(0.6, 15000) == 9000
+    assert oracle.budget_k(0.57, 100) == 57      # 0.57 * 100 = 56.999... in binary64
+    assert oracle.budget_k(0.29, 100) == 29
+    assert oracle.budget_k(0.0, 10) == 0 and oracle.budget_k(1.0, 10) == 10
+    assert oracle.budget_k(-3.0, 10) == 0 and oracle.budget_k(7.0, 10) == 10
+    with pytest.raises(ValueError):
+        oracle.budget_k(float("nan"), 10)
+
+
+def brute_keep(score, k):
+    s = np.where(np.isfinite(score), score, -np.inf)
+    n = len(s)
+    keep = np.zeros(n, np.uint8)
+    for j in range(n):
+        rank = sum(1 for l in range(n) if s[l] > s[j] or (s[l] == s[j] and l < j))
+        keep[j] = rank < k
+    return keep
+
+
+def test_topk_matches_brute_force_rank():
+    rng = np.random.default_rng(13)
+    p = random_small(13, "full", dtype="f32", n_req=3)
+    for trial in range(5):
+        sc = rng.integers(0, 12, size=p.N).astype(np.float64) / 7.0  # many exact ties
+        if trial == 3:
+            sc[::5] = np.nan
+            sc[1] = np.inf
+            sc[2] = -np.inf
+        keep, ks = oracle.topk(p, sc)
+        for b, (lo, hi) in enumerate(oracle.pool_bounds(p)):
+            np.testing.assert_array_equal(keep[lo:hi], brute_keep(sc[lo:hi], ks[b]))
+            assert keep[lo:hi].sum() == ks[b]
+
+
+def test_topk_k_zero_and_all_and_ties():
+    p = random_small(14, "full", dtype="f32", n_req=1)
+    n = p.N
+    sc = np.ones(n)
+    keep, _ = oracle.topk(p, sc, ratios=[0.0])
+    assert keep.sum() == 0
+    keep, _ = oracle.topk(p, sc, ratios=[1.0])
+    assert keep.sum() == n
+    keep, ks = oracle.topk(p, sc, ratios=[0.5])
+    assert keep[: ks[0]].all() and not keep[ks[0]:].any()
+
+
+# ---------------------------------------------------------------------------
+# Compaction.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mask", ["full", "causal", "blockdiag"])
+def test_compaction_numpy_equals_loop_and_invariants(mask):
+    p = random_small(21, mask, dtype="f32", n_req=3)
+    rng = np.random.default_rng(0)
+    keep = (rng.random(p.N) < 0.6).astype(np.uint8)
+    a = oracle.compact(p, keep, p.emb.numpy())
+    b = oracle.compact_loop(p, keep)
+    for key in ("token_idx", "spatial", "cu_seqlens", "img_counts"):
+        np.testing.assert_array_equal(a[key], b[key])
+    text = p.T - p.N
+    assert len(a["token_idx"]) == text + keep.sum()
+    for r in range(p.B):
+        seg = a["token_idx"][a["cu_seqlens"][r]:a["cu_seqlens"][r + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all((seg >= p.cu_seqlens[r]) & (seg < p.cu_seqlens[r + 1]))
+    np.testing.assert_array_equal(a["emb"], p.emb.numpy()[a["token_idx"]])
+    for s in range(p.S):
+        rows = a["spatial"][a["spatial"][:, 0] == s]
+        h, w = p.img_hw[s]
+        assert len(rows) == a["img_counts"][s]
+        assert np.all((rows[:, 1] < h) & (rows[:, 2] < w))
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each variant breaks one step of the arithmetic on the CPU
+# and at least one pin above must notice.
+# ---------------------------------------------------------------------------
+
+def _variant_segment_head(kind):
+    def f(q64, k64, seg, h, g, scale, causal, lse_given):
+        lo, hi, _b, loc, _glob = seg
+        n = hi - lo
+        Qs, Ks = q64[lo:hi, h, :], k64[lo:hi, g, :]
+        S = (1.0 if kind == "no_scale" else scale) * (Qs @ Ks.T)
+        if causal:
+            tri = np.arange(n)[None, :] <= np.arange(n)[:, None]
+            if kind == "causal_transposed":
+                tri = tri.T
+            S = np.where(tri, S, -np.inf)
+        m = S.max(axis=1)
+        lse_rows = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+        if lse_given is not None:
+            lse_rows = lse_given[lo:hi]
+        P = np.exp(S - lse_rows[:, None])
+        mass = (P.sum(axis=1) if kind == "row_sums" else P.sum(axis=0))[loc]
+        return lse_rows, mass
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "causal_transposed", "row_sums"])
+def test_planted_mistakes_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(O, "_segment_head", _variant_segment_head(kind))
+    caught = 0
+    for check in (test_two_keys_logistic_closed_form, test_zero_keys_causal_harmonic,
+                  lambda: test_mass_conservation_all_candidates("causal"),
+                  lambda: test_single_dominant_key(),
+                  lambda: test_mpmath_bruteforce_tiny("causal")):
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, kind
