@@ -1,0 +1,371 @@
+// C-ABI entry points: host-side validation, launch planning and dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "internal.h"
+
+namespace tsel {
+
+static thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+void clear_error() { g_err.clear(); }
+
+static int elem_size(int dt) { return dt == TSEL_F32 ? 4 : 2; }
+
+static int check_layout(const tsel_layout_t *l) {
+  if (l == nullptr) return fail(TSEL_EINVAL, "layout is NULL");
+  const int B = l->num_reqs, S = l->num_images, T = l->total_tokens;
+  if (B < 1) return fail(TSEL_EINVAL, "num_reqs must be >= 1 (got %d)", B);
+  if (S < 0 || T < 0) return fail(TSEL_EINVAL, "num_images and total_tokens must be >= 0");
+  if (!l->cu_seqlens_h || !l->cu_images_h || !l->cu_cands_h)
+    return fail(TSEL_EINVAL, "host layout arrays cu_seqlens_h/cu_images_h/cu_cands_h are required");
+  if (!l->cu_seqlens || !l->cu_images || !l->cu_cands)
+    return fail(TSEL_EINVAL, "device layout arrays cu_seqlens/cu_images/cu_cands are required");
+  if (S > 0 && (!l->img_start_h || !l->img_hw_h || !l->img_start || !l->img_hw))
+    return fail(TSEL_EINVAL, "img_start/img_hw (host and device) are required when num_images > 0");
+  const int32_t *cu = l->cu_seqlens_h, *ci = l->cu_images_h, *cc = l->cu_cands_h;
+  if (cu[0] != 0 || cu[B] != T) return fail(TSEL_EINVAL, "cu_seqlens must run from 0 to total_tokens");
+  if (ci[0] != 0 || ci[B] != S) return fail(TSEL_EINVAL, "cu_images must run from 0 to num_images");
+  if (cc[0] != 0) return fail(TSEL_EINVAL, "cu_cands[0] must be 0");
+  for (int b = 0; b < B; ++b) {
+    if (cu[b + 1] < cu[b]) return fail(TSEL_EINVAL, "cu_seqlens decreases at request %d", b);
+    if (ci[b + 1] < ci[b]) return fail(TSEL_EINVAL, "cu_images decreases at request %d", b);
+    int prev_end = cu[b];
+    for (int s = ci[b]; s < ci[b + 1]; ++s) {
+      const long long h = l->img_hw_h[2 * s], w = l->img_hw_h[2 * s + 1];
+      if (h <= 0 || w <= 0) return fail(TSEL_EINVAL, "image %d has an empty grid", s);
+      const long long start = l->img_start_h[s], end = start + h * w;
+      if (start < prev_end || end > cu[b + 1])
+        return fail(TSEL_EINVAL, "image %d is not sorted, disjoint and inside request %d", s, b);
+      if ((long long)cc[s + 1] - cc[s] != h * w)
+        return fail(TSEL_EINVAL, "cu_cands[%d+1]-cu_cands[%d] != rows*cols", s, s);
+      prev_end = (int)end;
+    }
+  }
+  return TSEL_OK;
+}
+
+static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
+  if (a == nullptr) return fail(TSEL_EINVAL, "attn is NULL");
+  if (a->dtype != TSEL_F32 && a->dtype != TSEL_F16 && a->dtype != TSEL_BF16)
+    return fail(TSEL_EUNSUPPORTED, "dtype %d is not supported", (int)a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 80 && a->head_dim != 96 && a->head_dim != 128)
+    return fail(TSEL_EUNSUPPORTED, "head_dim %d is not one of 64, 80, 96, 128", a->head_dim);
+  if (a->num_heads_q < 1 || a->num_heads_kv < 1 || a->num_heads_q % a->num_heads_kv != 0)
+    return fail(TSEL_EINVAL, "num_heads_q (%d) must be a positive multiple of num_heads_kv (%d)",
+                a->num_heads_q, a->num_heads_kv);
+  if (a->mask != TSEL_MASK_FULL && a->mask != TSEL_MASK_CAUSAL && a->mask != TSEL_MASK_BLOCKDIAG)
+    return fail(TSEL_EINVAL, "mask %d is not valid", (int)a->mask);
+  if (!isfinite(a->softmax_scale)) return fail(TSEL_EINVAL, "softmax_scale is not finite");
+  const int es = elem_size(a->dtype);
+  if (l->total_tokens > 0) {
+    if (a->q == nullptr || a->k == nullptr) return fail(TSEL_EINVAL, "q and k are required");
+    if (((uintptr_t)a->q | (uintptr_t)a->k) & 15) return fail(TSEL_EINVAL, "q and k must be 16-byte aligned");
+  }
+  const long long st[4] = {a->q_stride_tok, a->q_stride_head, a->k_stride_tok, a->k_stride_head};
+  for (long long s : st)
+    if (s <= 0 || (s * es) % 16 != 0)
+      return fail(TSEL_EINVAL, "q/k strides must be positive and multiples of 16 bytes");
+  if (a->mask == TSEL_MASK_BLOCKDIAG) {
+    const long long n = l->cu_cands_h[l->num_images];
+    if (n != l->total_tokens)
+      return fail(TSEL_EINVAL, "BLOCKDIAG needs every token inside an image (%lld of %d are)", n,
+                  l->total_tokens);
+  }
+  return TSEL_OK;
+}
+
+// Register budget of the resident operand: NT * KCH chunks of 16 (or 32) bytes
+// per lane must stay within 128 VGPRs.
+static int max_nt(int dtype, int D) {
+  const int kch = (D + 31) / 32;
+  const int vg_per_chunk = elem_size(dtype) * 2;
+  return (128 / (kch * vg_per_chunk)) >= 8 ? 8 : 4;
+}
+
+static void plan_common(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
+  const int hg = a->num_heads_q / a->num_heads_kv;
+  int F = 1;
+  while (F < 16 && hg % (F * 2) == 0) F *= 2;
+  p->dtype = a->dtype;
+  p->D = a->head_dim;
+  p->F = F;
+  p->nhb = a->num_heads_q / F;
+  p->segkind = (a->mask == TSEL_MASK_BLOCKDIAG) ? SEG_IMG : SEG_REQ;
+  p->nseg = (p->segkind == SEG_IMG) ? l->num_images : l->num_reqs;
+}
+
+static void seg_sizes(const tsel_layout_t *l, int kind, int a, long long &n, long long &nc) {
+  if (kind == SEG_REQ) {
+    n = l->cu_seqlens_h[a + 1] - l->cu_seqlens_h[a];
+    nc = l->cu_cands_h[l->cu_images_h[a + 1]] - l->cu_cands_h[l->cu_images_h[a]];
+  } else {
+    n = (long long)l->img_hw_h[2 * a] * l->img_hw_h[2 * a + 1];
+    nc = n;
+  }
+}
+
+int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
+  plan_common(a, l, p);
+  for (int nt = max_nt(a->dtype, a->head_dim); nt >= 4; nt -= 4) {
+    p->NT = nt;
+    p->TB = 4 * nt * 16 / p->F;
+    long long R = 0;
+    for (int s = 0; s < p->nseg; ++s) {
+      long long n, nc;
+      seg_sizes(l, p->segkind, s, n, nc);
+      R += (n + p->TB - 1) / p->TB;
+    }
+    p->jobs_per_hb = R;
+    p->total_jobs = R * p->nhb;
+    if (p->total_jobs >= 512) break;
+  }
+  p->KB = p->RC = p->RCmax = 0;
+  p->partial_bytes = 0;
+  if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
+  return TSEL_OK;
+}
+
+int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
+  plan_common(a, l, p);
+  long long maxn = 0;
+  for (int s = 0; s < p->nseg; ++s) {
+    long long n, nc;
+    seg_sizes(l, p->segkind, s, n, nc);
+    maxn = std::max(maxn, n);
+  }
+  for (int nt = max_nt(a->dtype, a->head_dim); nt >= 4; nt -= 4) {
+    p->NT = nt;
+    p->KB = 4 * nt * 16;
+    // Row chunk: ~8192 streamed rows per job, halved while the grid is small.
+    long long rc = std::max<long long>(16, 8192 / p->F);
+    for (;;) {
+      long long J = 0;
+      for (int s = 0; s < p->nseg; ++s) {
+        long long n, nc;
+        seg_sizes(l, p->segkind, s, n, nc);
+        J += ((nc + p->KB - 1) / p->KB) * ((n + rc - 1) / rc);
+      }
+      p->RC = (int)rc;
+      p->jobs_per_hb = J;
+      p->total_jobs = J * p->nhb;
+      if (p->total_jobs >= 1024 || rc < 32) break;
+      rc = (rc / 2 + 15) / 16 * 16;
+    }
+    if (p->total_jobs >= 512) break;
+  }
+  p->RCmax = (int)std::max<long long>(1, (maxn + p->RC - 1) / p->RC);
+  const long long N = l->cu_cands_h[l->num_images];
+  p->partial_bytes = (size_t)p->nhb * p->RCmax * N * sizeof(float);
+  if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
+  return TSEL_OK;
+}
+
+static DevLayout dev_layout(const tsel_layout_t *l) {
+  DevLayout L;
+  L.B = l->num_reqs;
+  L.S = l->num_images;
+  L.T = l->total_tokens;
+  L.cu_seqlens = l->cu_seqlens;
+  L.cu_images = l->cu_images;
+  L.img_start = l->img_start;
+  L.img_hw = l->img_hw;
+  L.cu_cands = l->cu_cands;
+  return L;
+}
+
+static AttnArgs attn_args(const tsel_attn_t *a, const tsel_layout_t *l, const AttnPlan &p) {
+  AttnArgs x{};
+  x.L = dev_layout(l);
+  x.q = a->q;
+  x.q_st = a->q_stride_tok;
+  x.q_sh = a->q_stride_head;
+  x.k = a->k;
+  x.k_st = a->k_stride_tok;
+  x.k_sh = a->k_stride_head;
+  x.hq = a->num_heads_q;
+  x.hg = a->num_heads_q / a->num_heads_kv;
+  x.F = p.F;
+  x.nhb = p.nhb;
+  x.causal = (a->mask == TSEL_MASK_CAUSAL) ? 1 : 0;
+  x.segkind = p.segkind;
+  x.nseg = p.nseg;
+  const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / sqrt((double)a->head_dim);
+  x.c1 = (float)(scale * 1.4426950408889634074);
+  x.jobs_per_hb = (int)p.jobs_per_hb;
+  x.total_jobs = (int)p.total_jobs;
+  x.TB = p.TB;
+  x.N = l->cu_cands_h[l->num_images];
+  x.RC = p.RC;
+  x.RCmax = p.RCmax;
+  x.KB = p.KB;
+  return x;
+}
+
+static size_t compact_ws(const tsel_layout_t *l) {
+  const long long nblk = (l->total_tokens + kCompactBlock - 1) / kCompactBlock;
+  return (size_t)((2 * nblk + 1) * sizeof(int) + 255) / 256 * 256;
+}
+
+}  // namespace tsel
+
+using namespace tsel;
+
+extern "C" {
+
+int tsel_version(void) { return TSEL_VERSION; }
+
+const char *tsel_last_error(void) { return g_err.c_str(); }
+
+size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t *layout) {
+  clear_error();
+  if (check_layout(layout) != TSEL_OK) return (size_t)-1;
+  switch (op) {
+    case TSEL_OP_LSE:
+      if (check_attn(attn, layout) != TSEL_OK) return (size_t)-1;
+      return 0;
+    case TSEL_OP_COLSCORE: {
+      if (check_attn(attn, layout) != TSEL_OK) return (size_t)-1;
+      AttnPlan p;
+      if (plan_colscore(attn, layout, &p) != TSEL_OK) return (size_t)-1;
+      return p.partial_bytes;
+    }
+    case TSEL_OP_TOPK:
+      return 0;
+    case TSEL_OP_COMPACT:
+      return compact_ws(layout);
+    default:
+      fail(TSEL_EINVAL, "unknown op %d", op);
+      return (size_t)-1;
+  }
+}
+
+int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc == TSEL_OK) rc = check_attn(attn, layout);
+  if (rc != TSEL_OK) return rc;
+  if (layout->total_tokens > 0 && lse == nullptr) return fail(TSEL_EINVAL, "lse is NULL");
+  if ((uintptr_t)lse & 3) return fail(TSEL_EINVAL, "lse must be 4-byte aligned");
+  AttnPlan p;
+  if ((rc = plan_lse(attn, layout, &p)) != TSEL_OK) return rc;
+  AttnArgs a = attn_args(attn, layout, p);
+  a.lse_out = lse;
+  const hipError_t e = launch_lse(p, a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_lse launch: %s", hipGetErrorString(e));
+  return TSEL_OK;
+}
+
+int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
+                  float *score, void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc == TSEL_OK) rc = check_attn(attn, layout);
+  if (rc != TSEL_OK) return rc;
+  const int N = layout->cu_cands_h[layout->num_images];
+  if (N == 0) return TSEL_OK;
+  if (lse == nullptr || score == nullptr) return fail(TSEL_EINVAL, "lse and score are required");
+  if (((uintptr_t)lse | (uintptr_t)score) & 3) return fail(TSEL_EINVAL, "lse/score must be 4-byte aligned");
+  AttnPlan p;
+  if ((rc = plan_colscore(attn, layout, &p)) != TSEL_OK) return rc;
+  if (p.partial_bytes > 0 && (workspace == nullptr || workspace_bytes < p.partial_bytes))
+    return fail(TSEL_EWORKSPACE, "tsel_colscore needs %zu workspace bytes (got %zu)", p.partial_bytes,
+                workspace_bytes);
+  if ((uintptr_t)workspace & 15) return fail(TSEL_EINVAL, "workspace must be 16-byte aligned");
+  AttnArgs a = attn_args(attn, layout, p);
+  a.lse_in = lse;
+  a.partial = reinterpret_cast<float *>(workspace);
+  const hipError_t e = launch_colscore(p, a, score, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_colscore launch: %s", hipGetErrorString(e));
+  return TSEL_OK;
+}
+
+int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const double *keep_ratio_h,
+                     int32_t *k_h, uint8_t *keep, void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc != TSEL_OK) return rc;
+  const int B = layout->num_reqs;
+  if (keep_ratio_h == nullptr || k_h == nullptr) return fail(TSEL_EINVAL, "keep_ratio_h and k_h are required");
+  for (int b = 0; b < B; ++b)
+    if (isnan(keep_ratio_h[b])) return fail(TSEL_EINVAL, "keep_ratio_h[%d] is NaN", b);
+  const int N = layout->cu_cands_h[layout->num_images];
+  if (N > 0 && (score == nullptr || keep == nullptr)) return fail(TSEL_EINVAL, "score and keep are required");
+  for (int b = 0; b < B; ++b) {
+    const long long nb = layout->cu_cands_h[layout->cu_images_h[b + 1]] -
+                         layout->cu_cands_h[layout->cu_images_h[b]];
+    const double r = std::min(1.0, std::max(0.0, keep_ratio_h[b]));
+    const long long k = (long long)floor(r * (double)nb + 1e-6);
+    k_h[b] = (int32_t)std::min(nb, std::max(0LL, k));
+  }
+  if (N == 0) return TSEL_OK;
+  const DevLayout L = dev_layout(layout);
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    TopkChunk ch;
+    ch.b0 = b0;
+    const int np = std::min(256, B - b0);
+    for (int i = 0; i < 256; ++i) ch.k[i] = (i < np) ? k_h[b0 + i] : 0;
+    const hipError_t e = launch_topk(L, score, ch, np, keep, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_budget_topk launch: %s", hipGetErrorString(e));
+  }
+  return TSEL_OK;
+}
+
+int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *emb,
+                 int64_t emb_stride, int64_t emb_row_bytes, int32_t out_capacity, void *out_emb,
+                 int64_t out_emb_stride, int32_t *out_token_idx, int32_t *out_spatial,
+                 int32_t *out_cu_seqlens, int32_t *out_img_counts, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc != TSEL_OK) return rc;
+  const int N = layout->cu_cands_h[layout->num_images];
+  if (N > 0 && keep == nullptr) return fail(TSEL_EINVAL, "keep is required");
+  if (out_capacity < 0) return fail(TSEL_EINVAL, "out_capacity must be >= 0");
+  if (out_capacity > 0 && out_token_idx == nullptr) return fail(TSEL_EINVAL, "out_token_idx is required");
+  if (emb != nullptr) {
+    if (out_emb == nullptr) return fail(TSEL_EINVAL, "out_emb is required when emb is given");
+    if (emb_row_bytes <= 0 || emb_stride < emb_row_bytes || out_emb_stride < emb_row_bytes)
+      return fail(TSEL_EINVAL, "embedding row bytes/strides are inconsistent");
+  }
+  const size_t need = compact_ws(layout);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(TSEL_EWORKSPACE, "tsel_compact needs %zu workspace bytes (got %zu)", need, workspace_bytes);
+  if ((uintptr_t)workspace & 3) return fail(TSEL_EINVAL, "workspace must be 4-byte aligned");
+  CompactArgs c{};
+  c.L = dev_layout(layout);
+  c.keep = keep;
+  c.N = N;
+  c.nblk = (layout->total_tokens + kCompactBlock - 1) / kCompactBlock;
+  int *ws = reinterpret_cast<int *>(workspace);
+  c.blk_cnt = ws;
+  c.blk_off = ws + c.nblk;
+  c.total = ws + 2 * c.nblk;
+  c.cap = out_capacity;
+  c.out_token_idx = out_token_idx;
+  c.out_spatial = out_spatial;
+  c.out_cu_seqlens = out_cu_seqlens;
+  c.out_img_counts = out_img_counts;
+  hipError_t e = launch_compact(c, (hipStream_t)stream);
+  if (e == hipSuccess && emb != nullptr)
+    e = launch_gather(emb, emb_stride, emb_row_bytes, out_emb, out_emb_stride, out_token_idx, c.total,
+                      out_capacity, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_compact launch: %s", hipGetErrorString(e));
+  return TSEL_OK;
+}
+
+}  // extern "C"

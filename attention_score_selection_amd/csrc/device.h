@@ -1,0 +1,107 @@
+// Device-side helpers: wave scans, layout lookups, workgroup-to-XCD mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace tsel {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// The hardware hands workgroup i to XCD i % 8.  Give each XCD one contiguous
+// range of job ids so that jobs sharing operands (same head block, same rows)
+// meet in the same L2.  `grid` is a multiple of 8.
+__device__ __forceinline__ int xcd_job(int bid, int grid) {
+  const int per = grid >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Token range of attention segment a.
+__device__ __forceinline__ void seg_tokens(const DevLayout &L, int kind, int a, int &lo, int &hi) {
+  if (kind == SEG_REQ) {
+    lo = L.cu_seqlens[a];
+    hi = L.cu_seqlens[a + 1];
+  } else {
+    lo = L.img_start[a];
+    hi = lo + L.img_hw[2 * a] * L.img_hw[2 * a + 1];
+  }
+}
+
+// Image range [s_lo, s_hi) and candidate range [c_lo, c_hi) of segment a.
+__device__ __forceinline__ void seg_images(const DevLayout &L, int kind, int a, int &s_lo, int &s_hi,
+                                           int &c_lo, int &c_hi) {
+  if (kind == SEG_REQ) {
+    s_lo = L.cu_images[a];
+    s_hi = L.cu_images[a + 1];
+  } else {
+    s_lo = a;
+    s_hi = a + 1;
+  }
+  c_lo = L.cu_cands[s_lo];
+  c_hi = L.cu_cands[s_hi];
+}
+
+// Largest index i in [lo, hi) with arr[i] <= x (arr sorted ascending);
+// returns lo - 1 if none.
+__device__ __forceinline__ int upper_index(const int *arr, int lo, int hi, int x) {
+  int a = lo, b = hi;  // answer in [a-1, b-1]
+  while (a < b) {
+    int mid = (a + b) >> 1;
+    if (arr[mid] <= x) a = mid + 1; else b = mid;
+  }
+  return a - 1;
+}
+
+// Token of candidate c, given the image range [s_lo, s_hi) that holds it.
+__device__ __forceinline__ int cand_token(const DevLayout &L, int s_lo, int s_hi, int c) {
+  int s = upper_index(L.cu_cands, s_lo, s_hi, c);
+  return L.img_start[s] + (c - L.cu_cands[s]);
+}
+
+// Find which segment owns item `idx` when segment a owns count(a) items,
+// segments in order.  Wave-uniform; all 64 lanes must call it.  Returns the
+// segment, and the item's index inside it in `local`; returns -1 if idx is
+// past the end.
+template <typename CountFn>
+__device__ __forceinline__ int find_segment(int nseg, int idx, CountFn count, int &local) {
+  const int lane = lane_id();
+  int base = 0;
+  for (int a0 = 0; a0 < nseg; a0 += 64) {
+    const int a = a0 + lane;
+    const int c = (a < nseg) ? count(a) : 0;
+    const int incl = wave_incl_scan(c);
+    const int total = __shfl(incl, 63, 64);
+    if (idx < base + total) {
+      const unsigned long long m = __ballot(base + incl > idx);
+      const int ln = __ffsll((long long)m) - 1;
+      local = idx - base - __shfl(incl - c, ln, 64);
+      return a0 + ln;
+    }
+    base += total;
+  }
+  local = 0;
+  return -1;
+}
+
+}  // namespace tsel

@@ -1,0 +1,92 @@
+// Internal declarations shared by the host layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "tsel.h"
+
+namespace tsel {
+
+// Layout as the kernels see it (device pointers, passed by value).
+struct DevLayout {
+  int B, S, T;
+  const int *cu_seqlens, *cu_images, *img_start, *img_hw, *cu_cands;
+};
+
+// How attention segments are formed: one per request (full / causal masks)
+// or one per image (block-diagonal mask).
+enum SegKind { SEG_REQ = 0, SEG_IMG = 1 };
+
+// Parameters of the LSE and column-score kernels.
+struct AttnArgs {
+  DevLayout L;
+  const void *q;
+  long long q_st, q_sh;  // element strides
+  const void *k;
+  long long k_st, k_sh;
+  int hq, hg;            // query heads, query heads per KV head
+  int F;                 // query heads folded into one 16-row tile (power of two dividing hg)
+  int nhb;               // head blocks = hq / F
+  int causal;            // 1 for TSEL_MASK_CAUSAL
+  int segkind;           // SegKind
+  int nseg;              // B or S
+  float c1;              // softmax scale * log2(e)
+  int jobs_per_hb;       // jobs of one head block
+  int total_jobs;        // nhb * jobs_per_hb
+  // LSE kernel
+  float *lse_out;
+  int TB;                // tokens per row block
+  // column-score kernel
+  const float *lse_in;
+  float *partial;        // [nhb][RCmax][N]
+  int N, RC, RCmax, KB;  // candidates, row-chunk tokens, max chunks per segment, keys per block
+};
+
+// Host-side plan of one attention launch.
+struct AttnPlan {
+  int dtype, D, NT;
+  int F, nhb, TB, KB, RC, RCmax;
+  int nseg, segkind;
+  long long jobs_per_hb, total_jobs;
+  size_t partial_bytes;
+};
+
+// Error reporting (thread-local message).
+int fail(int code, const char *fmt, ...);
+void clear_error();
+
+int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
+int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
+
+// Kernel launchers (attn.hip / select.hip).  Return hipError_t of the launch.
+hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, hipStream_t s);
+hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, float *score, hipStream_t s);
+
+struct TopkChunk {
+  int b0;        // first pool of this launch
+  int k[256];    // k of pools b0 .. b0+255
+};
+hipError_t launch_topk(const DevLayout &L, const float *score, const TopkChunk &ks, int npools,
+                       uint8_t *keep, hipStream_t s);
+
+struct CompactArgs {
+  DevLayout L;
+  const uint8_t *keep;
+  int N;
+  int nblk;
+  int *blk_cnt, *blk_off, *total;  // workspace
+  int cap;
+  int *out_token_idx, *out_spatial, *out_cu_seqlens, *out_img_counts;
+};
+hipError_t launch_compact(const CompactArgs &c, hipStream_t s);
+hipError_t launch_gather(const void *emb, long long emb_stride, long long row_bytes, void *out,
+                         long long out_stride, const int *token_idx, const int *total, int cap,
+                         hipStream_t s);
+
+constexpr int kCompactBlock = 1024;
+
+}  // namespace tsel

@@ -1,0 +1,180 @@
+/*
+ * tsel.h -- attention-score visual-token selection on AMD Instinct MI355X (gfx950).
+ *
+ * The selection step scores every vision token by the softmax attention it
+ * receives in one attention layer, keeps a global top-k of those scores over
+ * all images of a request, and compacts the kept tokens.  Four calls make up
+ * the path:
+ *
+ *   tsel_lse          per-row softmax log-sum-exp over all visible keys
+ *   tsel_colscore     tile-by-tile recomputation of P = exp(s - LSE), reduced
+ *                     down the candidate columns, averaged over heads and rows
+ *   tsel_budget_topk  one top-k per request pool, k = floor(r * N + 1e-6)
+ *   tsel_compact      stable compaction and gather of the kept tokens
+ *
+ * Sources: LiteVLM (arXiv 2506.07416) review, section 3.2 (token selection
+ * module) and its formula section (score of a vision token = the attention it
+ * receives; softmax(QK^T / sqrt(d))); REDtech "vision token compression + SERE"
+ * article, sections 3.1-3.2 (dominant tokens found by the average attention a
+ * token receives at a chosen layer, one global candidate pool per request,
+ * reuse of FlashAttention's softmax LSE, column-wise reduction without
+ * materialising the attention matrix, updated lengths / image boundaries /
+ * original spatial indices after pruning).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers without an _h suffix are DEVICE pointers; _h pointers are HOST
+ *   pointers read synchronously during the call.  The caller owns every
+ *   buffer; the library allocates no device memory.  Scratch space comes from
+ *   a caller workspace whose size tsel_workspace_size() reports.
+ * - Every call validates its host-side arguments first.  On failure it
+ *   returns a negative TSEL_E* code before enqueuing anything, and
+ *   tsel_last_error() (thread-local) describes the problem.  On success it
+ *   returns TSEL_OK after enqueuing its kernels on `stream` (a hipStream_t;
+ *   NULL is the null stream).  No call synchronises the device or copies
+ *   device memory to the host.
+ * - Device array contents are trusted to equal their host mirrors.
+ * - Results are deterministic: no floating-point atomics; every reduction
+ *   runs in a fixed order.
+ */
+#ifndef TSEL_H_
+#define TSEL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSEL_VERSION 1
+
+#define TSEL_OK 0
+#define TSEL_EINVAL (-1)      /* bad pointer, size, offset, ratio or layout        */
+#define TSEL_EUNSUPPORTED (-2) /* dtype or head_dim outside what is built          */
+#define TSEL_EWORKSPACE (-3)  /* workspace missing or smaller than required        */
+#define TSEL_EHIP (-4)        /* a HIP launch reported an error                    */
+
+typedef enum { TSEL_F32 = 0, TSEL_F16 = 1, TSEL_BF16 = 2 } tsel_dtype_t;
+
+/* Which keys a row sees (the LiteVLM first decoder layer is causal; the
+ * REDtech ViT-layer statistics use per-image bidirectional attention):
+ *   FULL       every token of the same request,
+ *   CAUSAL     tokens j <= i of the same request (diagonal included),
+ *   BLOCKDIAG  tokens of the same image; every token must belong to an image. */
+typedef enum { TSEL_MASK_FULL = 0, TSEL_MASK_CAUSAL = 1, TSEL_MASK_BLOCKDIAG = 2 } tsel_mask_t;
+
+/* Token layout of one batch.  Requests are packed back to back.  Images are
+ * disjoint token ranges [img_start[s], img_start[s] + rows*cols), sorted by
+ * start, each inside its request; request b owns images
+ * cu_images[b] .. cu_images[b+1]-1.  Candidates (the vision tokens that
+ * compete for the budget) are numbered in token order: image s holds
+ * candidates cu_cands[s] .. cu_cands[s+1]-1, cu_cands[s+1]-cu_cands[s] =
+ * rows*cols.  Every array is given twice: on the device and on the host. */
+typedef struct {
+  int32_t num_reqs;               /* B >= 1                                         */
+  int32_t num_images;             /* S >= 0                                         */
+  int32_t total_tokens;           /* T = cu_seqlens[B]                              */
+  const int32_t *cu_seqlens;      /* [B+1] device                                   */
+  const int32_t *cu_images;       /* [B+1] device                                   */
+  const int32_t *img_start;       /* [S]   device                                   */
+  const int32_t *img_hw;          /* [2S]  device, (rows, cols) per image           */
+  const int32_t *cu_cands;        /* [S+1] device                                   */
+  const int32_t *cu_seqlens_h;    /* host mirrors of the five arrays above          */
+  const int32_t *cu_images_h;
+  const int32_t *img_start_h;
+  const int32_t *img_hw_h;
+  const int32_t *cu_cands_h;
+} tsel_layout_t;
+
+/* One attention layer's queries and keys.  q is [T, Hq, head_dim] and k is
+ * [T, Hkv, head_dim] with arbitrary token and head strides (in ELEMENTS) and a
+ * contiguous last dimension.  Query head h reads KV head h / (Hq / Hkv).
+ * Requirements: Hq % Hkv == 0; head_dim in {64, 80, 96, 128}; q and k 16-byte
+ * aligned; both strides multiples of 16 bytes.  softmax_scale <= 0 selects
+ * 1/sqrt(head_dim) (LiteVLM review, formula section). */
+typedef struct {
+  tsel_dtype_t dtype;
+  int32_t num_heads_q;
+  int32_t num_heads_kv;
+  int32_t head_dim;
+  const void *q;
+  int64_t q_stride_tok, q_stride_head;
+  const void *k;
+  int64_t k_stride_tok, k_stride_head;
+  tsel_mask_t mask;
+  float softmax_scale;
+} tsel_attn_t;
+
+/* Workspace queries (op codes for tsel_workspace_size). */
+#define TSEL_OP_LSE 0
+#define TSEL_OP_COLSCORE 1
+#define TSEL_OP_TOPK 2
+#define TSEL_OP_COMPACT 3
+
+/* Bytes of workspace `op` needs for this problem (0 if none; the caller may
+ * then pass NULL).  `attn` may be NULL for TSEL_OP_TOPK / TSEL_OP_COMPACT.
+ * Returns (size_t)-1 when the arguments fail validation. */
+size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t *layout);
+
+/* Per-row softmax normaliser (natural log) over every key the row sees, text
+ * keys included -- the LSE a FlashAttention forward returns (REDtech article,
+ * section 3.2):  lse[h*T + i] = log sum_{j visible(i)} exp(scale * q_{i,h} . k_{j,g(h)}).
+ * Output: lse, fp32 [Hq, T] contiguous, every entry written.  Arithmetic:
+ * MFMA products in fp32, exp2/log2 in fp32.  Non-finite inputs give a
+ * non-finite LSE for the rows that see them.  No workspace. */
+int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, void *stream);
+
+/* Importance score of every candidate (LiteVLM review, formula section: the
+ * attention a vision token receives; REDtech article, section 3.2: the
+ * average attention it receives, computed tile by tile from the reused LSE
+ * without writing the attention matrix out):
+ *   score[c] = 1/(Hq * n_b) * sum_h sum_{i in request b, i sees c} exp(scale * q_{i,h}.k_{c,g(h)} - lse[h*T+i])
+ * where n_b is the length of c's request (all rows of the request count,
+ * masked pairs contribute zero).  lse: fp32 [Hq, T], either from tsel_lse or
+ * supplied by the caller (e.g. a FlashAttention forward).  Output: score,
+ * fp32 [N], N = cu_cands[S].  Workspace: tsel_workspace_size(TSEL_OP_COLSCORE). */
+int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
+                  float *score, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Global budget per request (REDtech article, sections 3.1-3.2: all images of
+ * a request compete in one pool; LiteVLM review, section 3.2 / section 5 table:
+ * keep ratio r).  For pool b with N_b candidates,
+ *   k_b = clamp(floor(clamp(r_b, 0, 1) * N_b + 1e-6), 0, N_b)      (binary64)
+ * and the k_b candidates with the largest scores are kept; equal scores go to
+ * the lower candidate index; NaN and +-inf scores rank as -inf.
+ * keep_ratio_h: host [B]; NaN is TSEL_EINVAL.  k_h: host [B], written
+ * synchronously.  keep: device uint8 [N], 1 = kept.  No workspace. */
+int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const double *keep_ratio_h,
+                     int32_t *k_h, uint8_t *keep, void *stream);
+
+/* Stable compaction of every request (REDtech article, section 3.2: new
+ * multimodal lengths, image boundaries and original spatial indices).  A
+ * token stays iff it is not a candidate (text always stays) or its keep flag
+ * is set; order is preserved.  With T_out = sum_b (n_b - N_b + k_b):
+ *   out_token_idx  int32 [T_out]     original packed token index
+ *   out_spatial    int32 [T_out, 3]  (image, row, col), (-1, -1, -1) for text
+ *   out_cu_seqlens int32 [B+1]       new packed offsets
+ *   out_img_counts int32 [S]         kept candidates per image
+ *   out_emb        [T_out] rows of emb_row_bytes bytes, copied bit-exact from
+ *                  emb (row t at emb + t*emb_stride bytes) to out_emb (row p at
+ *                  out_emb + p*out_emb_stride bytes); emb may be NULL to skip.
+ * out_capacity is the number of rows the output arrays hold; rows past it are
+ * not written (pass T_out computed from k_h).  Any output pointer but
+ * out_token_idx may be NULL.  Workspace: tsel_workspace_size(TSEL_OP_COMPACT). */
+int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *emb,
+                 int64_t emb_stride, int64_t emb_row_bytes, int32_t out_capacity, void *out_emb,
+                 int64_t out_emb_stride, int32_t *out_token_idx, int32_t *out_spatial,
+                 int32_t *out_cu_seqlens, int32_t *out_img_counts, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Description of the last error on this thread ("" if none). */
+const char *tsel_last_error(void);
+
+/* TSEL_VERSION of the built library. */
+int tsel_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TSEL_H_ */

@@ -102,32 +102,40 @@ def _segment_head(q64, k64, seg, h, g, scale, causal, lse_given):
     mass = np.zeros(len(loc))
     for r0 in range(0, n, ROW_BLOCK):
         r1 = min(n, r0 + ROW_BLOCK)
-        S = scale * (Qs[r0:r1] @ Ks.T)
+        # Causal rows r0..r1-1 see keys 0..r1-1 only; keys past r1 would be
+        # masked to -inf, so they are left out of the logits.
+        kend = r1 if causal else n
+        S = scale * (Qs[r0:r1] @ Ks[:kend].T)
         if causal:
             rows = np.arange(r0, r1)[:, None]
-            S = np.where(np.arange(n)[None, :] <= rows, S, -np.inf)
+            S = np.where(np.arange(kend)[None, :] <= rows, S, -np.inf)
         if lse_given is None:
             m = S.max(axis=1)
             lse_rows = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
         else:
             lse_rows = lse_given[lo + r0: lo + r1]
         lse_out[r0:r1] = lse_rows
-        if len(loc):
-            P = np.exp(S[:, loc] - lse_rows[:, None])
-            mass += P.sum(axis=0)
+        vis = loc < kend
+        if vis.any():
+            P = np.exp(S[:, loc[vis]] - lse_rows[:, None])
+            mass[vis] += P.sum(axis=0)
     return lse_out, mass
 
 
 def attention_stats(prob, lse_in: Optional[np.ndarray] = None, scale: Optional[float] = None,
-                    heads: Optional[Sequence[int]] = None, workers: int = 1):
+                    heads: Optional[Sequence[int]] = None, workers: int = 1,
+                    segments: Optional[Sequence[int]] = None):
     """Return ``(lse [Hq, T] float64, mass [N] float64)``.
 
     ``lse_in`` (``[Hq, T]``) switches to the supplied-LSE path: the rows'
     normaliser is taken from it instead of being computed.  ``heads``
     restricts the work to a subset of query heads (their LSE rows and their
-    share of the mass).  ``workers`` > 1 runs (segment, head) tasks on
-    threads; numpy's BLAS and ufuncs release the GIL, and the per-task
-    results are summed in a fixed order, so the answer does not depend on it.
+    share of the mass); ``segments`` to a subset of attention segments
+    (requests, or images under the block-diagonal mask).  Entries outside the
+    subset are NaN (LSE) or 0 (mass).  ``workers`` > 1 runs (segment, head)
+    tasks on threads; numpy's BLAS and ufuncs release the GIL, and the
+    per-task results are summed in a fixed order, so the answer does not
+    depend on it.
     """
     q64, k64 = to_f64(prob.q), to_f64(prob.k)
     hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
@@ -137,7 +145,8 @@ def attention_stats(prob, lse_in: Optional[np.ndarray] = None, scale: Optional[f
     causal = prob.mask == "causal"
     segs = attention_segments(prob)
     heads = list(range(hq)) if heads is None else list(heads)
-    tasks = [(si, h) for h in heads for si in range(len(segs))]
+    seg_ids = range(len(segs)) if segments is None else list(segments)
+    tasks = [(si, h) for h in heads for si in seg_ids]
     lse_in64 = None if lse_in is None else np.asarray(lse_in, np.float64)
 
     def run(task):
@@ -158,6 +167,26 @@ def attention_stats(prob, lse_in: Optional[np.ndarray] = None, scale: Optional[f
         lse[h, lo:hi] = lse_rows
         mass[glob] += m
     return lse, mass
+
+
+def lse_rows(prob, tokens: Sequence[int], scale: Optional[float] = None) -> np.ndarray:
+    """LSE of selected rows, every query head: ``[Hq, len(tokens)]`` float64.
+    Each row is the log-sum-exp of its visible logits, one row at a time."""
+    q64, k64 = to_f64(prob.q), to_f64(prob.k)
+    hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
+    rep = hq // hkv
+    scale = default_scale(d) if scale is None else scale
+    segs = attention_segments(prob)
+    out = np.full((hq, len(tokens)), np.nan)
+    for col, t in enumerate(tokens):
+        for lo, hi, _b, _loc, _glob in segs:
+            if lo <= t < hi:
+                kend = t + 1 if prob.mask == "causal" else hi
+                for h in range(hq):
+                    z = scale * (k64[lo:kend, h // rep, :] @ q64[t, h, :])
+                    m = z.max()
+                    out[h, col] = m + np.log(np.exp(z - m).sum())
+    return out
 
 
 def request_of_candidate(prob) -> np.ndarray:

@@ -1,0 +1,173 @@
+"""Host-side checks of the C-ABI library that need no GPU.
+
+The library must load and export every function ``include/tsel.h``
+declares, and its argument validation must reject bad input with the
+documented codes before it touches the HIP runtime.  Every call below fails
+validation, so no kernel is launched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from attention_score_selection_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsel.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from attention_score_selection_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tsel_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_path(lib):
+    names = declared_functions()
+    for n in ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact"):
+        assert n in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert lib.tsel_version() == 1
+
+
+FAKE = 4096  # non-null device address that validation never dereferences
+
+
+class HostLayout:
+    """A tsel_layout_t whose device fields hold placeholder addresses."""
+
+    def __init__(self, cu_seqlens, cu_images, img_start, img_hw, cu_cands):
+        self.h = [np.ascontiguousarray(np.asarray(a, np.int32).reshape(-1))
+                  for a in (cu_seqlens, cu_images, img_start, img_hw, cu_cands)]
+        c = B.CLayout()
+        c.num_reqs = len(self.h[0]) - 1
+        c.num_images = len(self.h[2])
+        c.total_tokens = int(self.h[0][-1])
+        for name, arr in zip(("cu_seqlens", "cu_images", "img_start", "img_hw", "cu_cands"), self.h):
+            setattr(c, name + "_h", arr.ctypes.data if arr.size else None)
+            setattr(c, name, FAKE if arr.size else None)
+        self.c = c
+
+
+def good_layout():
+    # two requests: [img 4x4 @0, text 3] and [text 2, img 2x3 @2, text 1]
+    return HostLayout([0, 19, 28], [0, 1, 2], [0, 21], [[4, 4], [2, 3]], [0, 16, 22])
+
+
+def attn(dtype=B.TSEL_BF16, hq=8, hkv=2, d=128, mask=1, q=FAKE, k=FAKE, st=None):
+    a = B.CAttn()
+    a.dtype, a.num_heads_q, a.num_heads_kv, a.head_dim = dtype, hq, hkv, d
+    a.q, a.k = q, k
+    a.q_stride_tok, a.q_stride_head = (st or (hq * d, d))
+    a.k_stride_tok, a.k_stride_head = hkv * d, d
+    a.mask, a.softmax_scale = mask, 0.0
+    return a
+
+
+def last_error(lib):
+    return lib.tsel_last_error().decode()
+
+
+def call_lse(lib, a, lay, out=FAKE):
+    return lib.tsel_lse(ctypes.byref(a), ctypes.byref(lay.c), out, None)
+
+
+def test_attn_validation_codes(lib):
+    lay = good_layout()
+    assert call_lse(lib, attn(d=72), lay) == B.TSEL_EUNSUPPORTED
+    assert "head_dim" in last_error(lib)
+    assert call_lse(lib, attn(dtype=7), lay) == B.TSEL_EUNSUPPORTED
+    assert call_lse(lib, attn(hq=6, hkv=4), lay) == B.TSEL_EINVAL
+    assert call_lse(lib, attn(q=FAKE + 8), lay) == B.TSEL_EINVAL
+    assert "aligned" in last_error(lib)
+    assert call_lse(lib, attn(st=(8 * 128 + 4, 128)), lay) == B.TSEL_EINVAL
+    assert call_lse(lib, attn(mask=5), lay) == B.TSEL_EINVAL
+    a = attn()
+    a.softmax_scale = float("nan")
+    assert call_lse(lib, a, lay) == B.TSEL_EINVAL
+    # BLOCKDIAG needs every token inside an image.
+    assert call_lse(lib, attn(mask=2), lay) == B.TSEL_EINVAL
+    assert "BLOCKDIAG" in last_error(lib)
+    assert lib.tsel_lse(None, ctypes.byref(lay.c), FAKE, None) == B.TSEL_EINVAL
+
+
+@pytest.mark.parametrize("bad", ["cu_end", "overlap", "outside", "cands", "empty_grid", "no_reqs"])
+def test_layout_validation(lib, bad):
+    args = dict(cu_seqlens=[0, 19, 28], cu_images=[0, 1, 2], img_start=[0, 21],
+                img_hw=[[4, 4], [2, 3]], cu_cands=[0, 16, 22])
+    if bad == "cu_end":
+        pass
+    elif bad == "overlap":
+        args.update(cu_images=[0, 2, 2], img_start=[0, 10], cu_seqlens=[0, 40, 49])
+    elif bad == "outside":
+        args["img_start"] = [0, 25]
+    elif bad == "cands":
+        args["cu_cands"] = [0, 16, 21]
+    elif bad == "empty_grid":
+        args["img_hw"] = [[4, 4], [0, 3]]
+    elif bad == "no_reqs":
+        args.update(cu_seqlens=[0], cu_images=[0], img_start=[], img_hw=[], cu_cands=[0])
+    lay = HostLayout(**args)
+    if bad == "cu_end":
+        lay.c.total_tokens = 30  # cu_seqlens must end at total_tokens
+    assert call_lse(lib, attn(), lay) == B.TSEL_EINVAL
+    assert last_error(lib)
+
+
+def test_topk_rejects_nan_ratio(lib):
+    lay = good_layout()
+    ratios = np.array([0.5, np.nan])
+    k_h = np.zeros(2, np.int32)
+    rc = lib.tsel_budget_topk(ctypes.byref(lay.c), FAKE, ratios.ctypes.data, k_h.ctypes.data, FAKE, None)
+    assert rc == B.TSEL_EINVAL and "NaN" in last_error(lib)
+
+
+def test_workspace_sizes_and_shortfall(lib):
+    lay = good_layout()
+    a = attn()
+    need = lib.tsel_workspace_size(B.TSEL_OP_COLSCORE, ctypes.byref(a), ctypes.byref(lay.c))
+    assert 0 < need < 1 << 30
+    assert need % 4 == 0
+    assert lib.tsel_workspace_size(B.TSEL_OP_LSE, ctypes.byref(a), ctypes.byref(lay.c)) == 0
+    assert lib.tsel_workspace_size(B.TSEL_OP_TOPK, None, ctypes.byref(lay.c)) == 0
+    comp = lib.tsel_workspace_size(B.TSEL_OP_COMPACT, None, ctypes.byref(lay.c))
+    assert comp >= 3 * 4
+    assert lib.tsel_workspace_size(9, None, ctypes.byref(lay.c)) == ctypes.c_size_t(-1).value
+    rc = lib.tsel_colscore(ctypes.byref(a), ctypes.byref(lay.c), FAKE, FAKE, FAKE, need - 4, None)
+    assert rc == B.TSEL_EWORKSPACE
+    rc = lib.tsel_compact(ctypes.byref(lay.c), FAKE, None, 0, 0, 10, None, 0, FAKE, None, None, None,
+                          FAKE, comp - 4, None)
+    assert rc == B.TSEL_EWORKSPACE
+
+
+def test_compact_rejects_inconsistent_embedding_args(lib):
+    lay = good_layout()
+    comp = lib.tsel_workspace_size(B.TSEL_OP_COMPACT, None, ctypes.byref(lay.c))
+    rc = lib.tsel_compact(ctypes.byref(lay.c), FAKE, FAKE, 64, 128, 10, FAKE, 128, FAKE, None, None,
+                          None, FAKE, comp, None)
+    assert rc == B.TSEL_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

@@ -34,11 +34,12 @@ def handmade(requests, q, k, mask, ratios=1.0, emb_dim=4):
     k = torch.as_tensor(np.asarray(k, np.float32))
     assert q.shape[0] == T and k.shape[0] == T
     B = len(cu) - 1
-    return Problem(name="hand", q=q, k=k, mask=mask, cu_seqlens=cu, cu_images=cui,
-                   img_start=st, img_hw=hw, cu_cands=cc,
-                   keep_ratio=np.broadcast_to(np.float64(ratios), (B,)).copy(),
-                   emb=torch.arange(T * emb_dim, dtype=torch.float32).reshape(T, emb_dim),
-                   dtype="f32")
+    p = Problem(name="hand", q=q, k=k, mask=mask, cu_seqlens=cu, cu_images=cui,
+                img_start=st, img_hw=hw, cu_cands=cc,
+                keep_ratio=np.broadcast_to(np.float64(ratios), (B,)).copy(),
+                emb_dim=emb_dim, emb_dtype="f32", dtype="f32")
+    p.emb = torch.arange(T * emb_dim, dtype=torch.float32).reshape(T, emb_dim)
+    return p
 
 
 def visible(prob, i, j):

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Small and medium randomized layouts and the three smaller named workloads
+are compared element by element with a live oracle run.  The two large
+workloads are checked at full size: the 16384-token GQA decoder layer
+against oracle scores stored by ``tests/golden/make_oracle_cache.py`` plus
+live per-row LSE samples, and the varlen batch with the oracle's own LSE
+supplied and live oracle masses for sampled requests.  Tolerances are
+documented in ``tests/parity.py``.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_score_selection_amd as tsel
+import oracle
+from workloads import make_config, make_problem, random_medium, random_small
+
+sys.path.insert(0, os.path.dirname(__file__))
+import parity as P  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    tsel.lib()  # raises if the library is not built
+    return torch.device("cuda:0")
+
+
+def announce(prob):
+    print(f"\n[case] {prob.name} T={prob.T} N={prob.N} Hq={prob.hq} Hkv={prob.hkv} d={prob.d} "
+          f"{prob.dtype} {prob.mask}", flush=True)
+
+
+SMALL = [(s, m, dt, hq, hkv, d) for s, (m, dt, hq, hkv, d) in enumerate([
+    ("full", "f32", 4, 4, 64), ("causal", "f32", 4, 2, 64), ("blockdiag", "f32", 2, 1, 128),
+    ("full", "bf16", 8, 2, 128), ("causal", "bf16", 4, 1, 80), ("blockdiag", "bf16", 6, 2, 96),
+    ("full", "f16", 3, 3, 96), ("causal", "f16", 16, 1, 64), ("blockdiag", "f16", 4, 4, 80),
+    ("causal", "bf16", 12, 4, 128), ("full", "bf16", 32, 2, 64), ("causal", "f32", 2, 2, 96),
+])]
+
+
+@pytest.mark.parametrize("seed,mask,dtype,hq,hkv,d", SMALL)
+def test_small_random(dev, seed, mask, dtype, hq, hkv, d):
+    prob = random_small(100 + seed, mask, dtype=dtype, hq=hq, hkv=hkv, d=d, n_req=3)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
+MEDIUM = [("causal", "bf16", 8, 1, 128), ("full", "f16", 16, 4, 80), ("blockdiag", "bf16", 4, 4, 64),
+          ("causal", "f32", 4, 2, 64), ("causal", "f16", 64, 8, 128), ("full", "bf16", 2, 2, 96)]
+
+
+@pytest.mark.parametrize("i", range(len(MEDIUM)))
+def test_medium_random(dev, i):
+    mask, dtype, hq, hkv, d = MEDIUM[i]
+    prob = random_medium(200 + i, mask, dtype=dtype, hq=hq, hkv=hkv, d=d, n_req=2 + i % 2)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, workers=oracle.default_workers(), with_emb=False),
+                 prob.emb)
+
+
+@pytest.mark.parametrize("cfg,std", [(1, None), (2, None), (2, 1.0), (3, None)])
+def test_named_workload_live_oracle(dev, cfg, std):
+    prob = make_config(cfg, seed=cfg if std is None else cfg + 100, std=std)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    ref = oracle.run(prob, workers=oracle.default_workers(), with_emb=False)
+    P.full_check(prob, got, ref, prob.emb)
+
+
+def test_decoder_16384_gqa_full_size(dev):
+    """Full-size GQA decoder layer: every score against the stored oracle
+    masses, the kept set, the compaction, and live LSE samples."""
+    cache = np.load(os.path.join(GOLDEN, "oracle_c4.npz"))
+    prob = make_config(4)
+    announce(prob)
+    assert input_digest(prob) == str(cache["digest"]), "regenerated inputs differ from the stored oracle's"
+    got = P.run_gpu(prob, dev)
+    ref_mass = cache["mass"]
+    P.check_scores(prob, got["score"], ref_mass)
+    ref_keep, ref_k = oracle.topk(prob, oracle.scores(prob, ref_mass))
+    assert np.array_equal(got["k"], ref_k)
+    exact = P.check_keep(prob, got["keep"], ref_mass, ref_k)
+    P.check_compaction_valid(prob, got["keep"], got["compact"], prob.emb)
+    if exact:
+        P.check_compaction_exact(prob, got["compact"], oracle.compact(prob, ref_keep), prob.emb)
+    rows = np.linspace(0, prob.T - 1, 24).astype(int)
+    ref_lse = oracle.lse_rows(prob, rows)
+    P.check_lse(prob, got["lse"][:, rows], ref_lse)
+
+
+def input_digest(prob):
+    import hashlib
+    h = hashlib.sha256()
+    for t in (prob.q, prob.k):
+        h.update(t.contiguous().view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()
+
+
+def test_varlen_supplied_lse_full_size(dev):
+    """Varlen batch with the LSE supplied (the oracle's, rounded to fp32):
+    sampled requests against live oracle masses, every pool and the
+    compaction checked for validity, plus the supplied-LSE shift identity."""
+    prob = make_config(5)
+    announce(prob)
+    workers = oracle.default_workers()
+    lse64, _ = oracle.attention_stats(prob, workers=workers)
+    lse32 = lse64.astype(np.float32)
+    got = P.run_gpu(prob, dev, lse=lse32)
+    sizes = np.diff(prob.cu_seqlens)
+    sample = [int(b) for b in np.argsort(sizes)[:2]]
+    _, ref_mass = oracle.attention_stats(prob, lse_in=lse32, workers=workers, segments=sample)
+    bounds = oracle.pool_bounds(prob)
+    cands = np.concatenate([np.arange(*bounds[b]) for b in sample])
+    P.check_scores(prob, got["score"], ref_mass, cands=cands)
+    ref_keep, ref_k = oracle.topk(prob, oracle.scores(prob, ref_mass))
+    assert np.array_equal(got["k"], ref_k)
+    P.check_keep(prob, got["keep"], ref_mass, ref_k, pools=sample)
+    P.check_compaction_valid(prob, got["keep"], got["compact"], prob.emb)
+    # Every pool: the GPU's kept set is a valid top-k of the GPU's scores.
+    for b, (lo, hi) in enumerate(bounds):
+        s, kp = got["score"][lo:hi], got["keep"][lo:hi].astype(bool)
+        if 0 < kp.sum() < hi - lo:
+            assert s[kp].min() >= s[~kp].max()
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_large_shapes_value_sensitive(dev, cfg):
+    """The decoder shapes at std 1 (peaked attention), reduced to 3 requests
+    / 4096 tokens so the live oracle stays fast."""
+    if cfg == 4:
+        imgs = [(i * 750, 25, 30) for i in range(4)]
+        prob = make_problem("decoder_4096_gqa64x8_std1", [(4096, imgs)], 64, 8, 128, "bf16",
+                            "causal", 1.0, 104, ratios=0.6, emb_dim=512)
+    else:
+        reqs = [(1500, [(0, 20, 30), (600, 16, 20)]), (900, [(0, 17, 23)]), (2100, [(0, 32, 32)])]
+        prob = make_problem("varlen_3req_h32_std1", reqs, 32, 32, 128, "f16", "causal", 1.0, 105,
+                            ratio_range=(0.5, 0.9), emb_dim=256)
+    announce(prob)
+    ref = oracle.run(prob, workers=oracle.default_workers(), with_emb=False)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, ref, prob.emb)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases.
+# ---------------------------------------------------------------------------
+
+def test_keep_nothing_and_everything(dev):
+    prob = random_small(31, "causal", dtype="bf16", hq=4, hkv=2, d=64, n_req=3)
+    prob.keep_ratio = np.array([0.0, 1.0, 0.5])
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+    lo, hi = oracle.pool_bounds(prob)[0]
+    assert got["keep"][lo:hi].sum() == 0
+    lo, hi = oracle.pool_bounds(prob)[1]
+    assert got["keep"][lo:hi].all()
+
+
+def test_exact_ties_keep_lowest_indices(dev):
+    """Zero keys under a full mask: every score is exactly 1/n; the budget
+    keeps the first k candidates of each pool."""
+    prob = random_small(32, "full", dtype="bf16", hq=4, hkv=2, d=64, n_req=2)
+    prob.k = torch.zeros_like(prob.k)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    for b, (lo, hi) in enumerate(oracle.pool_bounds(prob)):
+        n_b = prob.cu_seqlens[b + 1] - prob.cu_seqlens[b]
+        assert np.all(got["score"][lo:hi] == got["score"][lo])
+        assert abs(got["score"][lo] - 1.0 / n_b) <= 2e-3 / n_b
+        k = got["k"][b]
+        assert got["keep"][lo:lo + k].all() and not got["keep"][lo + k:hi].any()
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
+def test_empty_requests_and_imageless_requests(dev):
+    reqs = [(0, []), (37, [(5, 4, 6)]), (0, []), (20, []), (41, [(0, 3, 3), (12, 5, 5)]), (0, [])]
+    prob = make_problem("empties", reqs, 4, 2, 64, "bf16", "causal", 1.0, 33,
+                        ratio_range=(0.3, 0.8), emb_dim=24)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
+def test_tiny_images_blockdiag(dev):
+    reqs = [(1 + 4 + 2 + 9, [(0, 1, 1), (1, 2, 2), (5, 1, 2), (7, 3, 3)])]
+    prob = make_problem("tiny_images", reqs, 2, 1, 64, "f16", "blockdiag", 1.0, 34, ratios=0.5,
+                        emb_dim=8)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
+def test_nonfinite_inputs_rank_last(dev):
+    """A NaN in one query row poisons the LSE of that row and the scores of
+    every candidate the row sees; those rank as -inf, identically on both sides."""
+    prob = random_small(35, "causal", dtype="bf16", hq=2, hkv=1, d=64, n_req=2)
+    q = prob.q.clone()
+    t_bad = int(prob.cu_seqlens[1]) - 3  # late row of request 0
+    q[t_bad, 1, 5] = float("nan")
+    prob.q = q
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    ref = oracle.run(prob, with_emb=False)
+    assert np.array_equal(np.isnan(got["score"]), np.isnan(ref["score"]))
+    assert np.isnan(ref["score"]).any()
+    fin = np.isfinite(ref["score"])
+    rtol = P.rtol_of(prob)
+    assert np.all(np.abs(got["score"][fin] - ref["score"][fin]) <=
+                  np.maximum(rtol * np.abs(ref["score"][fin]), 1e-6))
+    assert np.array_equal(got["keep"], ref["keep"])
+
+
+def test_strided_qk_from_fused_projection(dev):
+    """Q and K as views into one fused [T, Hq + 2*Hkv, d] projection."""
+    prob = random_medium(36, "causal", dtype="bf16", hq=8, hkv=2, d=128, n_req=2)
+    announce(prob)
+    T = prob.T
+    qkv = torch.empty((T, 8 + 2 * 2, 128), dtype=torch.bfloat16)
+    qkv[:, :8] = prob.q
+    qkv[:, 8:10] = prob.k
+    qkv[:, 10:] = 0
+    lay = tsel.Layout.from_problem(prob, dev)
+    g = qkv.to(dev)
+    q, k = g[:, :8], g[:, 8:10]
+    lse = tsel.tsel_lse(q, k, lay, "causal")
+    score = tsel.tsel_colscore(q, k, lay, "causal", lse)
+    torch.cuda.synchronize()
+    ref = oracle.run(prob, with_emb=False)
+    P.check_lse(prob, lse.cpu().double().numpy(), ref["lse"])
+    P.check_scores(prob, score.cpu().double().numpy(), ref["mass"])
+
+
+def test_supplied_lse_shift_identity(dev):
+    """Supplying LSE + delta scales every score by exp(-delta) (reuse path)."""
+    prob = random_medium(37, "causal", dtype="f16", hq=4, hkv=4, d=128, n_req=2)
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    q, k = prob.q.to(dev), prob.k.to(dev)
+    lse = tsel.tsel_lse(q, k, lay, "causal")
+    s0 = tsel.tsel_colscore(q, k, lay, "causal", lse).double()
+    s1 = tsel.tsel_colscore(q, k, lay, "causal", (lse + 0.75).contiguous()).double()
+    torch.cuda.synchronize()
+    ratio = (s1 / s0).cpu().numpy()
+    assert np.allclose(ratio, np.exp(-0.75), rtol=1e-5)
+
+
+def test_deterministic_repeat(dev):
+    prob = random_medium(38, "causal", dtype="bf16", hq=16, hkv=4, d=128, n_req=3)
+    announce(prob)
+    a = P.run_gpu(prob, dev)
+    b = P.run_gpu(prob, dev)
+    assert np.array_equal(a["lse"], b["lse"], equal_nan=True)
+    assert np.array_equal(a["score"], b["score"])
+    assert np.array_equal(a["keep"], b["keep"])
+    for key in a["compact"]:
+        assert torch.equal(a["compact"][key], b["compact"][key])

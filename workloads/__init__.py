@@ -12,8 +12,11 @@ Recipe (numpy ``default_rng(seed)``, PCG64), in draw order:
 2. Q as standard normals in fp32, times ``std``,
 3. K the same way,
 4. dominant keys (tokens whose K is multiplied by 4 in every KV head),
-5. keep ratios (only the varlen batch draws them),
-6. embedding rows, standard normals.
+5. keep ratios (only the varlen batch draws them).
+
+Embedding rows (standard normals) come from their own stream,
+``default_rng([seed, 1])``, drawn on first use: a gather copies bytes, so
+the rows are only needed by the compaction checks and the benchmark.
 
 Q/K/emb are generated in fp32 and then rounded to the storage dtype with
 round-to-nearest-even (torch ``.to``), so every consumer reads the same
@@ -61,12 +64,27 @@ class Problem:
     img_hw: np.ndarray         # int32 [S, 2]  (rows, cols)
     cu_cands: np.ndarray       # int32 [S+1]
     keep_ratio: np.ndarray     # float64 [B]
-    emb: torch.Tensor          # [T, D]
+    emb_dim: int = 64
+    emb_dtype: str = "bf16"
     lse_supplied: bool = False
     seed: int = 0
     dtype: str = "bf16"
     std: float = 1.0
     dominant: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    _emb: Optional[torch.Tensor] = None
+
+    @property
+    def emb(self) -> torch.Tensor:
+        """Embedding rows [T, emb_dim] in ``emb_dtype`` (drawn on first use)."""
+        if self._emb is None:
+            rng = np.random.default_rng([self.seed, 1])
+            x = rng.standard_normal((self.T, self.emb_dim), dtype=np.float32)
+            self._emb = _round(x, self.emb_dtype)
+        return self._emb
+
+    @emb.setter
+    def emb(self, value: torch.Tensor):
+        self._emb = value
 
     @property
     def T(self) -> int:
@@ -171,12 +189,11 @@ def make_problem(name: str, requests, hq: int, hkv: int, d: int, dtype: str, mas
     else:
         lo, hi = ratio_range
         keep_ratio = rng.uniform(lo, hi, size=B)
-    edt = emb_dtype or dtype
-    emb = _round(rng.standard_normal((T, emb_dim), dtype=np.float32), edt)
     return Problem(name=name, q=_round(qf, dtype), k=_round(kf, dtype), mask=mask,
                    cu_seqlens=cu_seqlens, cu_images=cu_images, img_start=img_start,
-                   img_hw=img_hw, cu_cands=cu_cands, keep_ratio=keep_ratio, emb=emb,
-                   lse_supplied=lse_supplied, seed=seed, dtype=dtype, std=std, dominant=dom)
+                   img_hw=img_hw, cu_cands=cu_cands, keep_ratio=keep_ratio, emb_dim=emb_dim,
+                   emb_dtype=emb_dtype or dtype, lse_supplied=lse_supplied, seed=seed,
+                   dtype=dtype, std=std, dominant=dom)
 
 
 # ----------------------------------------------------------------------------
@@ -275,3 +292,26 @@ def random_small(seed: int, mask: str, dtype: str = "bf16", hq: int = 4, hkv: in
         reqs.append((length, images))
     return make_problem(f"small_{mask}_{dtype}_s{seed}", reqs, hq, hkv, d, dtype, mask, std,
                         seed, ratio_range=(0.2, 0.95), emb_dim=emb_dim, rng=rng)
+
+
+def random_medium(seed: int, mask: str, dtype: str = "bf16", hq: int = 8, hkv: int = 2,
+                  d: int = 128, n_req: int = 2, std: float = 1.0, emb_dim: int = 200,
+                  side=(8, 40), max_images: int = 4) -> Problem:
+    """Medium randomized layout (a few thousand tokens): several row blocks,
+    row chunks and key blocks of the GPU kernels, text prefixes, text between
+    images (except under the block-diagonal mask), ragged tails."""
+    rng = np.random.default_rng(seed)
+    reqs = []
+    for _ in range(n_req):
+        n_img = int(rng.integers(1, max_images + 1))
+        images, off = [], 0 if mask == "blockdiag" else int(rng.integers(0, 100))
+        for _ in range(n_img):
+            h, w = (int(x) for x in rng.integers(side[0], side[1] + 1, size=2))
+            images.append((off, h, w))
+            off += h * w
+            if mask != "blockdiag":
+                off += int(rng.integers(0, 120))
+        length = off if mask == "blockdiag" else off + int(rng.integers(1, 300))
+        reqs.append((length, images))
+    return make_problem(f"medium_{mask}_{dtype}_h{hq}x{hkv}_d{d}_s{seed}", reqs, hq, hkv, d, dtype,
+                        mask, std, seed, ratio_range=(0.3, 0.9), emb_dim=emb_dim, rng=rng)
