@@ -89,14 +89,6 @@ static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
   return TSEL_OK;
 }
 
-// Register budget of the resident operand: NT * KCH chunks of 16 (or 32) bytes
-// per lane must stay within 128 VGPRs.
-static int max_nt(int dtype, int D) {
-  const int kch = (D + 31) / 32;
-  const int vg_per_chunk = elem_size(dtype) * 2;
-  return (128 / (kch * vg_per_chunk)) >= 8 ? 8 : 4;
-}
-
 static void plan_common(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   const int hg = a->num_heads_q / a->num_heads_kv;
   int F = 1;
@@ -119,11 +111,14 @@ static void seg_sizes(const tsel_layout_t *l, int kind, int a, long long &n, lon
   }
 }
 
+// Row blocks of 4 waves x NG resident 32-row groups; fall back to one group
+// per wave when the grid would be small.
 int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
-  for (int nt = max_nt(a->dtype, a->head_dim); nt >= 4; nt -= 4) {
-    p->NT = nt;
-    p->TB = 4 * nt * 16 / p->F;
+  const int ng_max = max_groups(a->dtype, a->head_dim);
+  for (int ng = ng_max;; ng = 1) {
+    p->NT = ng;
+    p->TB = 4 * ng * 32 / p->F;
     long long R = 0;
     for (int s = 0; s < p->nseg; ++s) {
       long long n, nc;
@@ -132,7 +127,7 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     }
     p->jobs_per_hb = R;
     p->total_jobs = R * p->nhb;
-    if (p->total_jobs >= 512) break;
+    if (p->total_jobs >= 512 || ng == 1) break;
   }
   p->KB = p->RC = p->RCmax = 0;
   p->partial_bytes = 0;
@@ -140,6 +135,9 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   return TSEL_OK;
 }
 
+// Key blocks of 4 waves x NG resident 32-key groups; row chunks of ~8192
+// streamed rows, halved while the grid is small.  One partial per
+// (head block, row chunk, candidate).
 int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
   long long maxn = 0;
@@ -148,11 +146,11 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     seg_sizes(l, p->segkind, s, n, nc);
     maxn = std::max(maxn, n);
   }
-  for (int nt = max_nt(a->dtype, a->head_dim); nt >= 4; nt -= 4) {
-    p->NT = nt;
-    p->KB = 4 * nt * 16;
-    // Row chunk: ~8192 streamed rows per job, halved while the grid is small.
-    long long rc = std::max<long long>(16, 8192 / p->F);
+  const int ng_max = max_groups(a->dtype, a->head_dim);
+  for (int ng = ng_max;; ng = 1) {
+    p->NT = ng;
+    p->KB = 4 * ng * 32;
+    long long rc = std::max<long long>(32, 8192 / p->F);
     for (;;) {
       long long J = 0;
       for (int s = 0; s < p->nseg; ++s) {
@@ -163,11 +161,12 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
       p->RC = (int)rc;
       p->jobs_per_hb = J;
       p->total_jobs = J * p->nhb;
-      if (p->total_jobs >= 1024 || rc < 32) break;
-      rc = (rc / 2 + 15) / 16 * 16;
+      if (p->total_jobs >= 1024 || rc < 64) break;
+      rc = (rc / 2 + 31) / 32 * 32;
     }
-    if (p->total_jobs >= 512) break;
+    if (p->total_jobs >= 512 || ng == 1) break;
   }
+  p->TB = 0;
   p->RCmax = (int)std::max<long long>(1, (maxn + p->RC - 1) / p->RC);
   const long long N = l->cu_cands_h[l->num_images];
   p->partial_bytes = (size_t)p->nhb * p->RCmax * N * sizeof(float);

@@ -1,30 +1,34 @@
 // Softmax LSE and column-score kernels for gfx950.
 //
 // Both kernels share one shape: a RESIDENT operand held in VGPRs for the whole
-// workgroup lifetime (as the B operand of v_mfma_f32_16x16x32_{bf16,f16}, or
-// of eight v_mfma_f32_16x16x4_f32 for fp32), and a STREAMED operand that the
-// workgroup stages through LDS in tiles of 16 rows (the A operand).  The
-// 16x16 accumulator then holds, per lane, one column of the resident side
-// (lane % 16) and four rows of the streamed side (4 * (lane / 16) + r), so
-// every reduction the method needs along the streamed side happens inside the
-// lane; the four lane groups are combined once at the very end.
+// workgroup (the B operand of v_mfma_f32_32x32x16_{bf16,f16}, or of eight
+// v_mfma_f32_32x32x2_f32 for fp32), and a STREAMED operand that the workgroup
+// stages through LDS in tiles of 32 rows (the A operand).  The 32x32
+// accumulator then holds, per lane, one column of the resident side
+// (lane % 32) and sixteen rows of the streamed side, so every reduction the
+// method needs along the streamed side happens inside the lane; the two lane
+// halves are combined once at the very end.  The 32x32x16 shape is used
+// because on gfx950 it lets the VALU work (exp2, FMA, adds) overlap the matrix
+// pipe far better than 16x16x32 does.
 //
-//  * LSE (per-row softmax normaliser, REDtech article section 3.2 reuses it):
-//    resident = 128 query rows per wave, streamed = key tiles.  Rows reduce
+//  * LSE (per-row softmax normaliser; the REDtech article, section 3.2,
+//    reuses it): resident = query rows, streamed = key tiles.  Rows reduce
 //    in-lane.
-//  * Column score (attention a vision token receives, LiteVLM review formula
-//    section; column-wise reduction without materialising the attention
-//    matrix, REDtech article section 3.2): resident = 128 candidate keys per
-//    wave, streamed = query-row tiles together with their LSE.  Columns
-//    reduce in-lane; nothing of P leaves the registers.
+//  * Column score (attention a vision token receives: LiteVLM review,
+//    formula section; a column-wise reduction that never materialises the
+//    attention matrix: REDtech article, section 3.2): resident = candidate
+//    keys, streamed = query-row tiles with their LSE.  Columns reduce in-lane;
+//    nothing of P leaves the registers.
 //
-// Heads that share a KV head are folded into the row dimension (F heads per
-// tile row group), so one resident key fragment serves F query heads.
+// Query heads that share a KV head are folded into the row dimension (F heads
+// per token in each 32-row group), so one key fragment serves F query heads.
 //
-// The k-dimension of a 32-wide chunk is split over the four lane groups, 8
-// consecutive values each (16 B for 16-bit types).  For fp32 the same 8
-// values feed eight 16x16x4 steps; A and B use the same permutation of k, so
-// the contraction is unchanged.
+// A 16-wide k chunk is split over the two lane halves, 8 consecutive values
+// each (16 B for 16-bit types).  For fp32 the same 8 values feed eight 32x32x2
+// steps; A and B use the same permutation of k, so the contraction is
+// unchanged.
+#include <type_traits>
+
 #include "device.h"
 
 namespace tsel {
@@ -32,10 +36,12 @@ namespace tsel {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int DT> struct Elem { static constexpr int ES = 2; };
 template <> struct Elem<TSEL_F32> { static constexpr int ES = 4; };
 
+// 8 consecutive k values of one row: 16 B (16-bit types) or 32 B (fp32).
 template <int DT>
 struct Chunk {
   uint4 v[Elem<DT>::ES / 2];
@@ -55,45 +61,46 @@ __device__ __forceinline__ void load_chunk(Chunk<DT> &c, const char *p) {
 }
 
 template <int DT>
-__device__ __forceinline__ f32x4 mma(const Chunk<DT> &a, const Chunk<DT> &b, f32x4 acc);
+__device__ __forceinline__ f32x16 mma(const Chunk<DT> &a, const Chunk<DT> &b, f32x16 acc);
 
 template <>
-__device__ __forceinline__ f32x4 mma<TSEL_BF16>(const Chunk<TSEL_BF16> &a, const Chunk<TSEL_BF16> &b,
-                                                f32x4 acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[0]),
+__device__ __forceinline__ f32x16 mma<TSEL_BF16>(const Chunk<TSEL_BF16> &a, const Chunk<TSEL_BF16> &b,
+                                                 f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[0]),
                                                  __builtin_bit_cast(bf16x8, b.v[0]), acc, 0, 0, 0);
 }
 
 template <>
-__device__ __forceinline__ f32x4 mma<TSEL_F16>(const Chunk<TSEL_F16> &a, const Chunk<TSEL_F16> &b,
-                                               f32x4 acc) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a.v[0]),
+__device__ __forceinline__ f32x16 mma<TSEL_F16>(const Chunk<TSEL_F16> &a, const Chunk<TSEL_F16> &b,
+                                                f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a.v[0]),
                                                 __builtin_bit_cast(f16x8, b.v[0]), acc, 0, 0, 0);
 }
 
 template <>
-__device__ __forceinline__ f32x4 mma<TSEL_F32>(const Chunk<TSEL_F32> &a, const Chunk<TSEL_F32> &b,
-                                               f32x4 acc) {
+__device__ __forceinline__ f32x16 mma<TSEL_F32>(const Chunk<TSEL_F32> &a, const Chunk<TSEL_F32> &b,
+                                                f32x16 acc) {
   const f32x4v a0 = __builtin_bit_cast(f32x4v, a.v[0]), a1 = __builtin_bit_cast(f32x4v, a.v[1]);
   const f32x4v b0 = __builtin_bit_cast(f32x4v, b.v[0]), b1 = __builtin_bit_cast(f32x4v, b.v[1]);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[s], b0[s], acc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[s], b0[s], acc, 0, 0, 0);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[s], b1[s], acc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[s], b1[s], acc, 0, 0, 0);
   return acc;
 }
 
-// Geometry of one streamed 16-row tile in LDS.
+constexpr int kRows = 32;  // rows of a streamed tile and of a resident group
+
+// Geometry of one streamed 32-row tile in LDS.
 template <int DT, int D>
 struct Geom {
   static constexpr int ES = Elem<DT>::ES;
-  static constexpr int KCH = (D + 31) / 32;          // 32-wide k chunks
-  static constexpr int ROW = KCH * 32 * ES;          // bytes of a zero-padded row
-  static constexpr int RS = ROW + 16;                // LDS row stride (bank spread)
-  static constexpr int UNITS = ROW / 16;             // 16-byte units per row
-  static constexpr int UPT = (16 * UNITS + 255) / 256;  // units per thread (256 threads)
-  static constexpr int TILE = 16 * RS;               // bytes of one tile
-  static constexpr int VALID_UNITS = D * ES / 16;    // units that hold real data
+  static constexpr int KCH = D / 16;                   // 16-wide k chunks
+  static constexpr int ROW = D * ES;                   // bytes of a row
+  static constexpr int RS = ROW + 16;                  // LDS row stride (bank spread)
+  static constexpr int UNITS = ROW / 16;               // 16-byte units per row
+  static constexpr int UPT = (kRows * UNITS + 255) / 256;  // units per thread (256 threads)
+  static constexpr int TILE = kRows * RS;              // bytes of one tile
 };
 
 // Register staging of one streamed tile: global -> VGPR -> LDS.
@@ -109,10 +116,10 @@ struct Stage {
     for (int i = 0; i < G::UPT; ++i) {
       const int u = threadIdx.x + 256 * i;
       r[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (u < 16 * G::UNITS) {
+      if (u < kRows * G::UNITS) {
         const int row = u / G::UNITS, col = u % G::UNITS;
         const char *p = rowptr(row);
-        if (p != nullptr && col < G::VALID_UNITS) r[i] = *reinterpret_cast<const uint4 *>(p + col * 16);
+        if (p != nullptr) r[i] = *reinterpret_cast<const uint4 *>(p + col * 16);
       }
     }
   }
@@ -120,7 +127,7 @@ struct Stage {
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
       const int u = threadIdx.x + 256 * i;
-      if (u < 16 * G::UNITS) {
+      if (u < kRows * G::UNITS) {
         const int row = u / G::UNITS, col = u % G::UNITS;
         *reinterpret_cast<uint4 *>(tile + row * G::RS + col * 16) = r[i];
       }
@@ -128,39 +135,73 @@ struct Stage {
   }
 };
 
-// This lane's fragment (row lane%16, k values 32*kc + 8*(lane/16) .. +8) of
+// This lane's fragment (row lane%32, k values 16*kc + 8*(lane/32) .. +8) of
 // an LDS tile.
 template <int DT, int D>
-__device__ __forceinline__ void read_frag(Chunk<DT> (&f)[(D + 31) / 32], const char *tile) {
+__device__ __forceinline__ void read_frag(Chunk<DT> (&f)[D / 16], const char *tile) {
   using G = Geom<DT, D>;
   const int lane = lane_id();
-  const char *p = tile + (lane & 15) * G::RS + (lane >> 4) * 8 * G::ES;
+  const char *p = tile + (lane & 31) * G::RS + (lane >> 5) * 8 * G::ES;
 #pragma unroll
   for (int kc = 0; kc < G::KCH; ++kc) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p + kc * 32 * G::ES);
+    const uint4 *q = reinterpret_cast<const uint4 *>(p + kc * 16 * G::ES);
 #pragma unroll
     for (int i = 0; i < G::ES / 2; ++i) f[kc].v[i] = q[i];
   }
 }
 
-// Load the resident fragments of NT 16-row groups straight from global memory.
-template <int DT, int D, int NT, typename RowPtr>
-__device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NT][(D + 31) / 32], RowPtr rowptr) {
+// Load the resident fragments of NG 32-row groups straight from global memory.
+template <int DT, int D, int NG, typename RowPtr>
+__device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / 16], RowPtr rowptr) {
   using G = Geom<DT, D>;
   const int lane = lane_id();
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const char *p = rowptr(n * 16 + (lane & 15));
+  for (int n = 0; n < NG; ++n) {
+    const char *p = rowptr(n * kRows + (lane & 31));
 #pragma unroll
     for (int kc = 0; kc < G::KCH; ++kc) {
-      const int e = 32 * kc + 8 * (lane >> 4);
-      if (p != nullptr && e < D) load_chunk<DT>(res[n][kc], p + e * G::ES);
+      const int e = 16 * kc + 8 * (lane >> 5);
+      if (p != nullptr) load_chunk<DT>(res[n][kc], p + e * G::ES);
       else zero_chunk<DT>(res[n][kc]);
     }
   }
 }
 
+// acc[n] = A . R[n]^T for one streamed tile against all NG resident groups,
+// k chunks outermost so that the NG accumulation chains are independent.
+template <int DT, int D, int NG>
+__device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[D / 16],
+                                         const Chunk<DT> (&res)[NG][D / 16], f32x16 (&acc)[NG]) {
+#pragma unroll
+  for (int n = 0; n < NG; ++n) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[n][v] = 0.f;
+  }
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+#pragma unroll
+    for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[kc], res[n][kc], acc[n]);
+  }
+}
+
+// Row of the 32x32 accumulator held in register v by this lane.
+__device__ __forceinline__ int acc_row(int v) { return 8 * (v >> 2) + 4 * (lane_id() >> 5) + (v & 3); }
+
+// Sum of 16 values as a balanced tree (shorter dependency chains, smaller
+// rounding growth than a running sum).
+__device__ __forceinline__ float tree16(const float (&p)[16]) {
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = p[2 * i] + p[2 * i + 1];
+  return ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait until every outstanding vector-memory load of this wave has landed
+// (s_waitcnt vmcnt(0)); issued once after the resident operand is loaded so
+// that the streaming loop never waits on it.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPosInf = __builtin_huge_valf();
@@ -168,31 +209,30 @@ constexpr float kPosInf = __builtin_huge_valf();
 // ---------------------------------------------------------------------------
 // LSE kernel.
 // Job = (head block hb, segment a, row block rb): TB tokens x F heads of one
-// segment; each of the 4 waves owns NT*16 of those rows.  Keys stream in
-// tiles of 16 over [seg_lo, key_hi).
+// segment; each of the 4 waves owns NG*32 of those rows.  Keys stream in
+// tiles of 32 over [seg_lo, key_hi).
 // ---------------------------------------------------------------------------
 
 // One pass over key tiles [t0, t1).  MAXMODE: acc = running max of the raw
 // logit over this lane's keys.  Otherwise acc = running sum of
 // exp2(c1*s - m) over this lane's keys.
-template <int DT, int D, int NT, bool MAXMODE>
+template <int DT, int D, int NG, bool MAXMODE>
 __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, int key_lo,
                                          int key_hi, int t0, int t1,
-                                         const Chunk<DT> (&qf)[NT][(D + 31) / 32],
-                                         const int (&qtok)[NT], int wtok_min, int wtok_max,
-                                         const float (&m)[NT], float (&acc)[NT]) {
+                                         const Chunk<DT> (&qf)[NG][D / 16], const int (&qtok)[NG],
+                                         int wtok_min, int wtok_max, const float (&m)[NG],
+                                         float (&acc)[NG]) {
   using G = Geom<DT, D>;
-  const int lane = lane_id();
   const char *kbase = reinterpret_cast<const char *>(a.k);
   auto rowptr = [&](int it) {
     return [=](int r) -> const char * {
-      const int key = key_lo + 16 * it + r;
+      const int key = key_lo + kRows * it + r;
       if (key >= key_hi) return nullptr;
       return kbase + ((long long)key * a.k_st + (long long)g * a.k_sh) * G::ES;
     };
   };
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = MAXMODE ? kNegInf : 0.0f;
+  for (int n = 0; n < NG; ++n) acc[n] = MAXMODE ? kNegInf : 0.0f;
 
   Stage<DT, D> st;
   st.load(rowptr(t0));
@@ -201,43 +241,37 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
   __syncthreads();
   for (int it = t0; it < t1; ++it) {
     const char *tile = smem + ((it - t0) & 1) * G::TILE;
-    const int k0 = key_lo + 16 * it;
+    const int k0 = key_lo + kRows * it;
     if (!(a.causal && k0 > wtok_max)) {  // otherwise no row of this wave sees the tile
-    Chunk<DT> af[G::KCH];
-    read_frag<DT, D>(af, tile);
-    const bool need_mask = (k0 + 16 > key_hi) || (a.causal && k0 + 15 > wtok_min);
-    const int kl = k0 + 4 * (lane >> 4);  // this lane's keys: kl + r
+      Chunk<DT> af[G::KCH];
+      read_frag<DT, D>(af, tile);
+      f32x16 s[NG];
+      tile_mma<DT, D, NG>(af, qf, s);
+      // Keys past the segment end or (causal) past a row's token are invisible.
+      auto epi = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NG; ++n) {
+          float p[16];
 #pragma unroll
-      for (int kc = 0; kc < G::KCH; ++kc) s = mma<DT>(af[kc], qf[n][kc], s);
-      if (MAXMODE) {
-        float v[4];
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + acc_row(v);
+            const bool vis = !MASKED || (key < key_hi && (!a.causal || key <= qtok[n]));
+            if (MAXMODE) p[v] = vis ? s[n][v] : kNegInf;
+            else p[v] = vis ? fast_exp2(fmaf(s[n][v], a.c1, -m[n])) : 0.0f;
+          }
+          if (MAXMODE) {
+            float t = p[0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = s[r];
-          if (need_mask) {
-            const int key = kl + r;
-            const bool vis = key < key_hi && (!a.causal || key <= qtok[n]);
-            v[r] = vis ? v[r] : kNegInf;
+            for (int v = 1; v < 16; ++v) t = fmaxf(t, p[v]);
+            acc[n] = fmaxf(acc[n], t);
+          } else {
+            acc[n] += tree16(p);
           }
         }
-        acc[n] = fmaxf(acc[n], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-      } else {
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = fast_exp2(fmaf(s[r], a.c1, -m[n]));
-          if (need_mask) {
-            const int key = kl + r;
-            const bool vis = key < key_hi && (!a.causal || key <= qtok[n]);
-            p[r] = vis ? p[r] : 0.0f;
-          }
-        }
-        acc[n] += (p[0] + p[1]) + (p[2] + p[3]);
-      }
-    }
+      };
+      if ((k0 + kRows > key_hi) || (a.causal && k0 + kRows - 1 > wtok_min)) epi(std::true_type{});
+      else epi(std::false_type{});
     }
     if (it + 1 < t1) {
       st.store(smem + ((it + 1 - t0) & 1) * G::TILE);
@@ -247,7 +281,7 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
   }
 }
 
-template <int DT, int D, int NT>
+template <int DT, int D, int NG>
 __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
   using G = Geom<DT, D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::TILE];
@@ -272,79 +306,63 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
   const int tok_lo = seg_lo + rb * TB;
   const int tok_hi = min(tok_lo + TB, seg_hi);
 
-  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int F = a.F;
-  const int wtok0 = tok_lo + w * (NT * 16 / F);
-  const int wtok_max = wtok0 + NT * 16 / F - 1;
+  const int wtok0 = tok_lo + w * (NG * kRows / F);
+  const int wtok_max = wtok0 + NG * kRows / F - 1;
   const int h0 = hb * F;
   const int g = h0 / a.hg;
   const int key_lo = seg_lo;
   const int key_hi = a.causal ? tok_hi : seg_hi;
-  const int ntiles = (key_hi - key_lo + 15) / 16;
+  const int ntiles = (key_hi - key_lo + kRows - 1) / kRows;
 
   // Resident queries: row q of this wave is (token wtok0 + q / F, head h0 + q % F).
-  Chunk<DT> qf[NT][G::KCH];
-  int qtok[NT];
+  Chunk<DT> qf[NG][G::KCH];
+  int qtok[NG];
   const char *qbase = reinterpret_cast<const char *>(a.q);
-  load_resident<DT, D, NT>(qf, [&](int q) -> const char * {
+  load_resident<DT, D, NG>(qf, [&](int q) -> const char * {
     const int t = wtok0 + q / F;
     if (t >= tok_hi) return nullptr;
     return qbase + ((long long)t * a.q_st + (long long)(h0 + q % F) * a.q_sh) * G::ES;
   });
 #pragma unroll
-  for (int n = 0; n < NT; ++n) qtok[n] = wtok0 + (n * 16 + (lane & 15)) / F;
+  for (int n = 0; n < NG; ++n) qtok[n] = wtok0 + (n * kRows + (lane & 31)) / F;
+  wait_vmem();
 
   // Offset m: max logit of the first key tile (which every row sees) plus 32
   // (log2 units); the sum pass then cannot overflow unless a later logit
   // exceeds it by ~100, which the check below catches.
-  float m[NT], acc[NT];
+  float m[NG], acc[NG];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) m[n] = 0.f;
+  for (int n = 0; n < NG; ++n) m[n] = 0.f;
   if (threadIdx.x == 0) s_bad = 0;
-  lse_pass<DT, D, NT, true>(smem, a, g, key_lo, key_hi, 0, 1, qf, qtok, wtok0, wtok_max, m, acc);
+  lse_pass<DT, D, NG, true>(smem, a, g, key_lo, key_hi, 0, 1, qf, qtok, wtok0, wtok_max, m, acc);
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float mx = acc[n];
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    m[n] = mx * a.c1 + 32.0f;
-  }
-  lse_pass<DT, D, NT, false>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
-  float tot[NT];
+  for (int n = 0; n < NG; ++n) m[n] = fmaxf(acc[n], __shfl_xor(acc[n], 32, 64)) * a.c1 + 32.0f;
+  lse_pass<DT, D, NG, false>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
+  float tot[NG];
   bool ok = true;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float v = acc[n];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    tot[n] = v;
-    if (qtok[n] < tok_hi) ok = ok && (v <= 0x1p100f) && (v >= 0x1p-100f);  // false for NaN
+  for (int n = 0; n < NG; ++n) {
+    tot[n] = acc[n] + __shfl_xor(acc[n], 32, 64);
+    if (qtok[n] < tok_hi) ok = ok && (tot[n] <= 0x1p100f) && (tot[n] >= 0x1p-100f);  // false for NaN
   }
   if (!ok) s_bad = 1;
   __syncthreads();
   if (s_bad) {
     // Exact two-pass fallback: true row max, then the sum against it.
-    lse_pass<DT, D, NT, true>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
+    lse_pass<DT, D, NG, true>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float mx = acc[n];
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m[n] = mx * a.c1;
-    }
-    lse_pass<DT, D, NT, false>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
+    for (int n = 0; n < NG; ++n) m[n] = fmaxf(acc[n], __shfl_xor(acc[n], 32, 64)) * a.c1;
+    lse_pass<DT, D, NG, false>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m,
+                               acc);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float v = acc[n];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      tot[n] = v;
-    }
+    for (int n = 0; n < NG; ++n) tot[n] = acc[n] + __shfl_xor(acc[n], 32, 64);
   }
-  if ((lane >> 4) == 0) {
+  if (lane < 32) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int q = n * 16 + lane;
+    for (int n = 0; n < NG; ++n) {
+      const int q = n * kRows + lane;
       const int t = wtok0 + q / F;
       if (t < tok_hi) {
         const float lse2 = m[n] + __log2f(tot[n]);
@@ -357,14 +375,14 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Column-score kernel.
 // Job = (head block hb, segment a, row chunk rc, key block kb).  Each wave
-// holds NT*16 candidate keys; query-row tiles of 16 rows (16/F tokens x F
+// holds NG*32 candidate keys; query-row tiles of 32 rows (32/F tokens x F
 // heads) and their LSE stream through LDS; per-column partial sums go to
 // partial[(hb*RCmax + rc)*N + c].
 // ---------------------------------------------------------------------------
-template <int DT, int D, int NT>
+template <int DT, int D, int NG>
 __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   using G = Geom<DT, D>;
-  constexpr int BUF = G::TILE + 64;  // tile + 16 floats of LSE (log2 units)
+  constexpr int BUF = G::TILE + kRows * 4;  // tile + 32 floats of LSE (log2 units)
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
@@ -389,36 +407,39 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   const int kb1 = min(kb0 + KB, c_hi);
   const int chunk_lo = seg_lo + rc * RC;
   const int chunk_hi = min(chunk_lo + RC, seg_hi);
-  const int first_ktok = cand_token(a.L, s_lo, s_hi, kb0);
+  const int first_ktok = __builtin_amdgcn_readfirstlane(cand_token(a.L, s_lo, s_hi, kb0));
   const int row_lo = a.causal ? max(chunk_lo, first_ktok) : chunk_lo;
   if (row_lo >= chunk_hi) return;  // no row of this chunk sees any key of the block
 
-  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int F = a.F;
   const int h0 = hb * F;
   const int g = h0 / a.hg;
-  const int wc0 = kb0 + w * NT * 16;
-  const int wlast = min(wc0 + NT * 16, kb1) - 1;
-  // Largest key token of this wave (candidates are in token order).
-  const int wkmax = (wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wlast) : -1;
-  const int wkmin = (wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wc0) : 0x7fffffff;
+  const int wc0 = kb0 + w * NG * kRows;
+  const int wlast = min(wc0 + NG * kRows, kb1) - 1;
+  // Smallest and largest key token of this wave (candidates are in token order).
+  const int wkmax = __builtin_amdgcn_readfirstlane(
+      (wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wlast) : -1);
+  const int wkmin = __builtin_amdgcn_readfirstlane(
+      (wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wc0) : 0x7fffffff);
 
-  // Resident keys.
-  Chunk<DT> kf[NT][G::KCH];
-  int ktok[NT];
+  // Resident keys: group n, lane column lane % 32 is candidate wc0 + 32n + lane % 32.
+  Chunk<DT> kf[NG][G::KCH];
+  int ktok[NG];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int c = wc0 + n * 16 + (lane & 15);
+  for (int n = 0; n < NG; ++n) {
+    const int c = wc0 + n * kRows + (lane & 31);
     ktok[n] = (c < kb1) ? cand_token(a.L, s_lo, s_hi, c) : 0x7fffffff;
   }
   const char *kbase = reinterpret_cast<const char *>(a.k);
-  load_resident<DT, D, NT>(kf, [&](int j) -> const char * {
-    const int t = ktok[j >> 4];
+  load_resident<DT, D, NG>(kf, [&](int j) -> const char * {
+    const int t = ktok[j / kRows];
     if (t == 0x7fffffff) return nullptr;
     return kbase + ((long long)t * a.k_st + (long long)g * a.k_sh) * G::ES;
   });
+  wait_vmem();
 
-  const int tpt = 16 / F;  // tokens per streamed tile
+  const int tpt = kRows / F;  // tokens per streamed tile
   const int ntiles = (chunk_hi - row_lo + tpt - 1) / tpt;
   const char *qbase = reinterpret_cast<const char *>(a.q);
   const long long T = a.L.T;
@@ -432,69 +453,76 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   auto lse_load = [&](int it) -> float {
     const int r = threadIdx.x;
     const int t = row_lo + it * tpt + r / F;
-    if (t >= chunk_hi) return kPosInf;
+    if (t >= chunk_hi) return kPosInf;  // padding rows contribute exp2(-inf) = 0
     return a.lse_in[(long long)(h0 + r % F) * T + t] * 1.44269504088896340736f;
   };
 
-  float cs[NT];
+  float cs[NG];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) cs[n] = 0.f;
+  for (int n = 0; n < NG; ++n) cs[n] = 0.f;
 
   Stage<DT, D> st;
   float lreg = 0.f;
   st.load(rowptr(0));
-  if (threadIdx.x < 16) lreg = lse_load(0);
+  if (threadIdx.x < kRows) lreg = lse_load(0);
   st.store(smem);
-  if (threadIdx.x < 16) reinterpret_cast<float *>(smem + G::TILE)[threadIdx.x] = lreg;
+  if (threadIdx.x < kRows) reinterpret_cast<float *>(smem + G::TILE)[threadIdx.x] = lreg;
   if (ntiles > 1) {
     st.load(rowptr(1));
-    if (threadIdx.x < 16) lreg = lse_load(1);
+    if (threadIdx.x < kRows) lreg = lse_load(1);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const char *buf = smem + (it & 1) * BUF;
     const int tt0 = row_lo + it * tpt;
     if (!(a.causal && tt0 + tpt - 1 < wkmin)) {  // otherwise every row precedes every key
-    Chunk<DT> af[G::KCH];
-    read_frag<DT, D>(af, buf);
-    const f32x4v l4 = *reinterpret_cast<const f32x4v *>(buf + G::TILE + 16 * (lane >> 4));
-    const bool need_mask = a.causal && tt0 < wkmax;
-    int rtok[4];
+      Chunk<DT> af[G::KCH];
+      read_frag<DT, D>(af, buf);
+      // LSE of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3.
+      float l2[16];
+      const float *lb = reinterpret_cast<const float *>(buf + G::TILE) + 4 * (lane >> 5);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rtok[r] = tt0 + (4 * (lane >> 4) + r) / F;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < G::KCH; ++kc) s = mma<DT>(af[kc], kf[n][kc], s);
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(fmaf(s[r], a.c1, -l4[r]));
-        if (need_mask) p[r] = (ktok[n] <= rtok[r]) ? p[r] : 0.0f;
+        for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
       }
-      cs[n] += (p[0] + p[1]) + (p[2] + p[3]);
-    }
+      f32x16 s[NG];
+      tile_mma<DT, D, NG>(af, kf, s);
+      // Causal: a row sees a key only if the key's token is not later.
+      auto epi = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+        for (int n = 0; n < NG; ++n) {
+          float p[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            p[v] = fast_exp2(fmaf(s[n][v], a.c1, -l2[v]));
+            if (MASKED) p[v] = (ktok[n] <= tt0 + acc_row(v) / F) ? p[v] : 0.0f;
+          }
+          cs[n] += tree16(p);
+        }
+      };
+      if (a.causal && tt0 < wkmax) epi(std::true_type{});
+      else epi(std::false_type{});
     }
     if (it + 1 < ntiles) {
       char *nb = smem + ((it + 1) & 1) * BUF;
       st.store(nb);
-      if (threadIdx.x < 16) reinterpret_cast<float *>(nb + G::TILE)[threadIdx.x] = lreg;
+      if (threadIdx.x < kRows) reinterpret_cast<float *>(nb + G::TILE)[threadIdx.x] = lreg;
       if (it + 2 < ntiles) {
         st.load(rowptr(it + 2));
-        if (threadIdx.x < 16) lreg = lse_load(it + 2);
+        if (threadIdx.x < kRows) lreg = lse_load(it + 2);
       }
     }
     __syncthreads();
   }
   float *out = a.partial + ((long long)hb * a.RCmax + rc) * a.N;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float v = cs[n];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    const int c = wc0 + n * 16 + (lane & 15);
-    if ((lane >> 4) == 0 && c < kb1) out[c] = v;
+  for (int n = 0; n < NG; ++n) {
+    const float v = cs[n] + __shfl_xor(cs[n], 32, 64);
+    const int c = wc0 + n * kRows + (lane & 31);
+    if (lane < 32 && c < kb1) out[c] = v;
   }
 }
 
@@ -521,60 +549,54 @@ __global__ __launch_bounds__(256) void colscore_finalize(AttnArgs a, float *scor
 }
 
 // ---------------------------------------------------------------------------
-// Launchers.
+// Launchers.  NG (resident 32-row groups per wave) is NGMAX<DT, D> or 1.
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int DT, int D, int NT>
+template <int DT, int D>
+constexpr int kNGMax = max_groups(DT, D);
+
+template <int DT, int D, int NG>
 hipError_t lse_go(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   const int grid = (int)((p.total_jobs + 7) / 8 * 8);
-  hipLaunchKernelGGL((lse_kernel<DT, D, NT>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((lse_kernel<DT, D, NG>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int D, int NT>
+template <int DT, int D, int NG>
 hipError_t col_go(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   const int grid = (int)((p.total_jobs + 7) / 8 * 8);
-  hipLaunchKernelGGL((colscore_kernel<DT, D, NT>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((colscore_kernel<DT, D, NG>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// Eight resident 16-row groups fit the register budget except for fp32 with
-// head_dim > 64, which only gets the four-group variant.
 template <int DT, int D>
-constexpr bool kWide = !(DT == TSEL_F32 && D > 64);
-
-template <int DT, int D>
-hipError_t lse_nt(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
-  if constexpr (kWide<DT, D>) {
-    if (p.NT == 8) return lse_go<DT, D, 8>(p, a, s);
-  }
-  return lse_go<DT, D, 4>(p, a, s);
+hipError_t lse_ng(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+  if (p.NT == kNGMax<DT, D>) return lse_go<DT, D, kNGMax<DT, D>>(p, a, s);
+  return lse_go<DT, D, 1>(p, a, s);
 }
 template <int DT, int D>
-hipError_t col_nt(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
-  if constexpr (kWide<DT, D>) {
-    if (p.NT == 8) return col_go<DT, D, 8>(p, a, s);
-  }
-  return col_go<DT, D, 4>(p, a, s);
+hipError_t col_ng(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+  if (p.NT == kNGMax<DT, D>) return col_go<DT, D, kNGMax<DT, D>>(p, a, s);
+  return col_go<DT, D, 1>(p, a, s);
 }
 
 template <int DT>
 hipError_t lse_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   switch (p.D) {
-    case 64: return lse_nt<DT, 64>(p, a, s);
-    case 80: return lse_nt<DT, 80>(p, a, s);
-    case 96: return lse_nt<DT, 96>(p, a, s);
-    default: return lse_nt<DT, 128>(p, a, s);
+    case 64: return lse_ng<DT, 64>(p, a, s);
+    case 80: return lse_ng<DT, 80>(p, a, s);
+    case 96: return lse_ng<DT, 96>(p, a, s);
+    default: return lse_ng<DT, 128>(p, a, s);
   }
 }
 template <int DT>
 hipError_t col_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   switch (p.D) {
-    case 64: return col_nt<DT, 64>(p, a, s);
-    case 80: return col_nt<DT, 80>(p, a, s);
-    case 96: return col_nt<DT, 96>(p, a, s);
-    default: return col_nt<DT, 128>(p, a, s);
+    case 64: return col_ng<DT, 64>(p, a, s);
+    case 80: return col_ng<DT, 80>(p, a, s);
+    case 96: return col_ng<DT, 96>(p, a, s);
+    default: return col_ng<DT, 128>(p, a, s);
   }
 }
 

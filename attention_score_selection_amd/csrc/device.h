@@ -95,8 +95,9 @@ __device__ __forceinline__ int find_segment(int nseg, int idx, CountFn count, in
     if (idx < base + total) {
       const unsigned long long m = __ballot(base + incl > idx);
       const int ln = __ffsll((long long)m) - 1;
-      local = idx - base - __shfl(incl - c, ln, 64);
-      return a0 + ln;
+      // Wave-uniform results: keep them in scalar registers.
+      local = __builtin_amdgcn_readfirstlane(idx - base - __shfl(incl - c, ln, 64));
+      return __builtin_amdgcn_readfirstlane(a0 + ln);
     }
     base += total;
   }

@@ -89,4 +89,12 @@ hipError_t launch_gather(const void *emb, long long emb_stride, long long row_by
 
 constexpr int kCompactBlock = 1024;
 
+// Resident 32-row groups per wave for a (dtype, head_dim): one group holds
+// (head_dim/16) x 8 values per lane; the total must leave room for the
+// accumulators within 256 VGPRs (two waves per SIMD).
+constexpr int max_groups(int dtype, int head_dim) {
+  const int per_group = (head_dim / 16) * (dtype == TSEL_F32 ? 4 : 2) * 2;  // VGPRs
+  return per_group <= 20 ? 4 : per_group <= 32 ? 3 : per_group <= 48 ? 2 : 1;
+}
+
 }  // namespace tsel

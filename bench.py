@@ -1,0 +1,173 @@
+"""Benchmark of the attention-score token-selection path on one MI355X.
+
+One step = the whole path over one batch already resident in HBM:
+tsel_lse -> tsel_colscore -> tsel_budget_topk -> tsel_compact (with the
+embedding-row gather), on the 16384-token GQA decoder-layer workload
+(64 query heads / 8 KV heads, head_dim 128, bf16, causal, 15000 vision
+tokens in 20 images of 25x30 plus 1384 text tokens, keep 60%, 5120-dim bf16
+hidden states gathered).
+
+Prints one JSON line.  ``value`` is score elements per second of the whole
+step: visible (head, row, vision-column) pairs divided by the step time.
+The ``roofline`` object describes the dominant kernel (timed with HIP events
+on the stream it runs on); ``cpu_baseline`` is the fp64 CPU oracle timed on
+a bounded sample of the same workload (one KV group's 8 query heads).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def visible_pairs(prob):
+    """Visible (head, row, candidate) pairs of the column-score step and
+    (head, row, key) pairs of the LSE step, from the layout alone."""
+    import numpy as np
+    cols = keys = 0
+    cu, ci, st, hw = prob.cu_seqlens, prob.cu_images, prob.img_start, prob.img_hw
+    for b in range(prob.B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        n = hi - lo
+        if prob.mask == "causal":
+            keys += n * (n + 1) // 2
+            for s in range(ci[b], ci[b + 1]):
+                t = np.arange(st[s], st[s] + hw[s, 0] * hw[s, 1]) - lo
+                cols += int((n - t).sum())
+        elif prob.mask == "full":
+            keys += n * n
+            cols += n * int(sum(hw[s, 0] * hw[s, 1] for s in range(ci[b], ci[b + 1])))
+        else:
+            for s in range(ci[b], ci[b + 1]):
+                m = int(hw[s, 0] * hw[s, 1])
+                keys += m * m
+                cols += m * m
+    return cols * prob.hq, keys * prob.hq
+
+
+def cpu_baseline(prob, elems_per_head):
+    """The oracle as it stands, on one KV group's query heads."""
+    import oracle
+    workers = oracle.default_workers()
+    heads = list(range(prob.hq // prob.hkv))
+    t0 = time.perf_counter()
+    oracle.attention_stats(prob, heads=heads, workers=workers)
+    dt = time.perf_counter() - t0
+    elems = elems_per_head * len(heads)
+    return {"value": elems / dt, "unit": "score elements/s", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 LSE + column mass of query heads 0-{len(heads) - 1} "
+                      f"(one KV group, {elems:.4g} elements) of the same workload, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the selection path "
+                                   "has no multi-GPU code (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_score_selection_amd as tsel
+    from workloads import make_config
+
+    prob = make_config(4)
+    dev = torch.device("cuda:0")
+    lay = tsel.Layout.from_problem(prob, dev)
+    q, k, emb = prob.q.to(dev), prob.k.to(dev), prob.emb.to(dev)
+    ratios = prob.keep_ratio
+    col_elems, lse_elems = visible_pairs(prob)
+    d = prob.d
+
+    # Preallocated outputs and workspaces: the timed loop allocates nothing.
+    lse = torch.empty((prob.hq, prob.T), dtype=torch.float32, device=dev)
+    score = torch.empty((prob.N,), dtype=torch.float32, device=dev)
+    keep = torch.empty((prob.N,), dtype=torch.uint8, device=dev)
+    ws_col = torch.empty((max(16, tsel.tsel_workspace_size(1, lay, q, k, prob.mask)),),
+                         dtype=torch.uint8, device=dev)
+    ws_cmp = torch.empty((tsel.tsel_workspace_size(3, lay),), dtype=torch.uint8, device=dev)
+    _, ks = tsel.tsel_budget_topk(lay, tsel.tsel_colscore(q, k, lay, prob.mask,
+                                                          tsel.tsel_lse(q, k, lay, prob.mask)), ratios)
+    outs = {}
+    tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
+    t_out = int(outs["token_idx"].numel())
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        tsel.tsel_lse(q, k, lay, prob.mask, out=lse)
+        if ev: ev[1].record(stream)
+        tsel.tsel_colscore(q, k, lay, prob.mask, lse, out=score, workspace=ws_col)
+        if ev: ev[2].record(stream)
+        tsel.tsel_budget_topk(lay, score, ratios, out=keep)
+        if ev: ev[3].record(stream)
+        tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events]) / 1e3
+    t_lse, t_col, t_topk, t_cmp = phase.mean(axis=0)
+    ms_per_step = wall / args.steps * 1e3
+
+    col_flops = 2.0 * d * col_elems
+    lse_flops = 2.0 * d * lse_elems
+    dominant = ("tsel_colscore", t_col, col_flops) if t_col >= t_lse else ("tsel_lse", t_lse, lse_flops)
+    achieved = dominant[2] / dominant[1] / 1e12
+    kept = int(np.sum(ks))
+    row_bytes = prob.emb_dim * emb.element_size()
+    gather_bytes = 2 * t_out * row_bytes + 16 * t_out + prob.N + 4 * prob.N
+    result = {
+        "metric": "score elements/s (H*Lq*Lk visible pairs) of the whole selection step",
+        "value": col_elems / (ms_per_step / 1e3),
+        "unit": "score elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded normal Q/K, std 1/sqrt(d); normal embeddings)",
+        "config": {"workload": prob.name, "tokens": prob.T, "heads_q": prob.hq, "heads_kv": prob.hkv,
+                   "head_dim": d, "mask": prob.mask, "vision_candidates": prob.N, "images": prob.S,
+                   "keep_ratio": float(ratios[0]), "kept_vision": kept, "tokens_out": t_out,
+                   "emb_dim": prob.emb_dim, "lse": "computed in-library"},
+        "phases_ms": {"lse": t_lse * 1e3, "colscore": t_col * 1e3, "budget_topk": t_topk * 1e3,
+                      "compact_gather": t_cmp * 1e3},
+        "colscore_elements_per_s": col_elems / t_col,
+        "colscore_mfma_frac": col_flops / t_col / 1e12 / PEAK_BF16_TFLOPS,
+        "lse_elements_per_s": lse_elems / t_lse,
+        "lse_mfma_frac": lse_flops / t_lse / 1e12 / PEAK_BF16_TFLOPS,
+        "kept_tokens_per_s": kept / (t_topk + t_cmp),
+        "select_gather_GBps": gather_bytes / (t_topk + t_cmp) / 1e9,
+        "roofline": {"kernel": dominant[0], "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(prob, col_elems / prob.hq)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
