@@ -53,6 +53,30 @@ def visible_pairs(prob):
     return cols * prob.hq, keys * prob.hq
 
 
+def kernel_source_digest() -> str:
+    """sha256 of the kernel sources, to tie stored counter data to a build."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_score_selection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when the summary is missing or was taken from other sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
+
+
 def cpu_baseline(prob, elems_per_head):
     """The oracle as it stands, on one KV group's query heads."""
     import oracle
@@ -73,11 +97,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB once (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the selection path "
-                                   "has no multi-GPU code (see the sharding notes in DESIGN.md)",
+                                   "has no multi-GPU code",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -162,8 +188,17 @@ def main():
         "select_gather_GBps": gather_bytes / (t_topk + t_cmp) / 1e9,
         "roofline": {"kernel": dominant[0], "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": stored_traffic(prob.name, dominant[0])},
     }
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        result["calib_copy_bytes"] = n
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prob, col_elems / prob.hq)
     print(json.dumps(result), flush=True)
