@@ -89,6 +89,19 @@ static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
   return TSEL_OK;
 }
 
+// The kernels address each streamed 32-row tile (and a tile's LSE values)
+// with 32-bit byte offsets from a per-tile base; those offsets must stay below
+// kBufferLimit.
+static int check_offsets(const tsel_attn_t *a, const tsel_layout_t *l, int F) {
+  const long long es = elem_size(a->dtype);
+  const long long k_span = 32LL * a->k_stride_tok * es;
+  const long long q_span = ((32LL / F) * a->q_stride_tok + (long long)F * a->q_stride_head) * es;
+  const long long l_span = ((long long)F * l->total_tokens + 32) * 4;
+  if (k_span >= kBufferLimit || q_span >= kBufferLimit || l_span >= kBufferLimit)
+    return fail(TSEL_EUNSUPPORTED, "strides too large: a 32-row tile spans 2 GiB or more");
+  return TSEL_OK;
+}
+
 static void plan_common(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   const int hg = a->num_heads_q / a->num_heads_kv;
   int F = 1;
@@ -115,6 +128,7 @@ static void seg_sizes(const tsel_layout_t *l, int kind, int a, long long &n, lon
 // per wave when the grid would be small.
 int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
+  if (int rc = check_offsets(a, l, p->F)) return rc;
   const int ng_max = max_groups(a->dtype, a->head_dim);
   for (int ng = ng_max;; ng = 1) {
     p->NT = ng;
@@ -140,6 +154,7 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
 // (head block, row chunk, candidate).
 int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
+  if (int rc = check_offsets(a, l, p->F)) return rc;
   long long maxn = 0;
   for (int s = 0; s < p->nseg; ++s) {
     long long n, nc;

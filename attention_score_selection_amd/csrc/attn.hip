@@ -103,33 +103,57 @@ struct Geom {
   static constexpr int TILE = kRows * RS;              // bytes of one tile
 };
 
-// Register staging of one streamed tile: global -> VGPR -> LDS.
+// Buffer offset past every valid byte: a load there returns zero.  Host-side
+// planning guarantees that all in-tile offsets stay below it.
+constexpr int kOOB = kBufferLimit;
+
+// Buffer resource for raw (unstructured) loads from `base`; on gfx9 parts the
+// third word selects 32-bit data format so that offset range checking applies.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, kOOB, 0x00020000);
+}
+
+// Register staging of one streamed tile: global -> VGPR -> LDS.  Each thread
+// moves UPT fixed 16-byte units of the tile; their byte offsets from the
+// tile's first row are computed once, so a step costs one compare and one
+// select per unit.  Units of rows past the valid range read as zero.
 template <int DT, int D>
 struct Stage {
   using G = Geom<DT, D>;
   uint4 r[G::UPT];
+  int off[G::UPT];  // byte offset of unit i from the tile base
+  int row[G::UPT];  // tile row of unit i (kRows: the unit is past the tile)
 
-  // rowptr(row) returns the global address of a row, or nullptr (zero row).
-  template <typename RowPtr>
-  __device__ __forceinline__ void load(RowPtr rowptr) {
+  // rowoff(row): byte offset of tile row `row` from the tile base.
+  template <typename RowOff>
+  __device__ __forceinline__ void init(RowOff rowoff) {
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
       const int u = threadIdx.x + 256 * i;
-      r[i] = make_uint4(0u, 0u, 0u, 0u);
       if (u < kRows * G::UNITS) {
-        const int row = u / G::UNITS, col = u % G::UNITS;
-        const char *p = rowptr(row);
-        if (p != nullptr) r[i] = *reinterpret_cast<const uint4 *>(p + col * 16);
+        row[i] = u / G::UNITS;
+        off[i] = rowoff(row[i]) + (u % G::UNITS) * 16;
+      } else {
+        row[i] = kRows;
+        off[i] = kOOB;
       }
     }
+  }
+  // Tile rows [0, nvalid) come from `base` (wave-uniform), the rest are zero.
+  __device__ __forceinline__ void load(const char *base, int nvalid) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base);
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i)
+      r[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, row[i] < nvalid ? off[i] : kOOB, 0, 0));
   }
   __device__ __forceinline__ void store(char *tile) const {
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
       const int u = threadIdx.x + 256 * i;
       if (u < kRows * G::UNITS) {
-        const int row = u / G::UNITS, col = u % G::UNITS;
-        *reinterpret_cast<uint4 *>(tile + row * G::RS + col * 16) = r[i];
+        const int rr = u / G::UNITS, col = u % G::UNITS;
+        *reinterpret_cast<uint4 *>(tile + rr * G::RS + col * 16) = r[i];
       }
     }
   }
@@ -223,21 +247,19 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
                                          int wtok_min, int wtok_max, const float (&m)[NG],
                                          float (&acc)[NG]) {
   using G = Geom<DT, D>;
-  const char *kbase = reinterpret_cast<const char *>(a.k);
-  auto rowptr = [&](int it) {
-    return [=](int r) -> const char * {
-      const int key = key_lo + kRows * it + r;
-      if (key >= key_hi) return nullptr;
-      return kbase + ((long long)key * a.k_st + (long long)g * a.k_sh) * G::ES;
-    };
-  };
+  // Key tile it: rows key_lo + 32*it + r of KV head g; rows from key_hi on are zero.
+  const char *kbase = reinterpret_cast<const char *>(a.k) + (long long)g * a.k_sh * G::ES;
+  const long long krow = a.k_st * G::ES;
+  auto tile_base = [&](int it) { return kbase + (long long)(key_lo + kRows * it) * krow; };
+  auto tile_rows = [&](int it) { return key_hi - (key_lo + kRows * it); };
 #pragma unroll
   for (int n = 0; n < NG; ++n) acc[n] = MAXMODE ? kNegInf : 0.0f;
 
   Stage<DT, D> st;
-  st.load(rowptr(t0));
+  st.init([&](int r) { return r * (int)krow; });
+  st.load(tile_base(t0), tile_rows(t0));
   st.store(smem);
-  if (t0 + 1 < t1) st.load(rowptr(t0 + 1));
+  if (t0 + 1 < t1) st.load(tile_base(t0 + 1), tile_rows(t0 + 1));
   __syncthreads();
   for (int it = t0; it < t1; ++it) {
     const char *tile = smem + ((it - t0) & 1) * G::TILE;
@@ -275,7 +297,7 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
     }
     if (it + 1 < t1) {
       st.store(smem + ((it + 1 - t0) & 1) * G::TILE);
-      if (it + 2 < t1) st.load(rowptr(it + 2));
+      if (it + 2 < t1) st.load(tile_base(it + 2), tile_rows(it + 2));
     }
     __syncthreads();
   }
@@ -301,12 +323,16 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
   if (seg < 0) return;
   int seg_lo, seg_hi;
   seg_tokens(a.L, a.segkind, seg, seg_lo, seg_hi);
+  // Layout values of this job are workgroup-uniform: keep them in scalar
+  // registers (tile addresses built from them then stay scalar too).
+  seg_lo = uni(seg_lo);
+  seg_hi = uni(seg_hi);
   const int nrb = (seg_hi - seg_lo + TB - 1) / TB;
   const int rb = a.causal ? nrb - 1 - local : local;  // causal: heaviest row blocks first
   const int tok_lo = seg_lo + rb * TB;
   const int tok_hi = min(tok_lo + TB, seg_hi);
 
-  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id(), w = uni(threadIdx.x >> 6);
   const int F = a.F;
   const int wtok0 = tok_lo + w * (NG * kRows / F);
   const int wtok_max = wtok0 + NG * kRows / F - 1;
@@ -401,27 +427,33 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   int seg_lo, seg_hi, s_lo, s_hi, c_lo, c_hi;
   seg_tokens(a.L, a.segkind, seg, seg_lo, seg_hi);
   seg_images(a.L, a.segkind, seg, s_lo, s_hi, c_lo, c_hi);
+  // Layout values of this job are workgroup-uniform: keep them in scalar
+  // registers (tile addresses built from them then stay scalar too).
+  seg_lo = uni(seg_lo);
+  seg_hi = uni(seg_hi);
+  s_lo = uni(s_lo);
+  s_hi = uni(s_hi);
+  c_lo = uni(c_lo);
+  c_hi = uni(c_hi);
   const int nkb = (c_hi - c_lo + KB - 1) / KB;
   const int rc = local / nkb, kb = local % nkb;
   const int kb0 = c_lo + kb * KB;
   const int kb1 = min(kb0 + KB, c_hi);
   const int chunk_lo = seg_lo + rc * RC;
   const int chunk_hi = min(chunk_lo + RC, seg_hi);
-  const int first_ktok = __builtin_amdgcn_readfirstlane(cand_token(a.L, s_lo, s_hi, kb0));
-  const int row_lo = a.causal ? max(chunk_lo, first_ktok) : chunk_lo;
+  const int first_ktok = uni(cand_token(a.L, s_lo, s_hi, kb0));
+  const int row_lo = uni(a.causal ? max(chunk_lo, first_ktok) : chunk_lo);
   if (row_lo >= chunk_hi) return;  // no row of this chunk sees any key of the block
 
-  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = lane_id(), w = uni(threadIdx.x >> 6);
   const int F = a.F;
   const int h0 = hb * F;
   const int g = h0 / a.hg;
   const int wc0 = kb0 + w * NG * kRows;
   const int wlast = min(wc0 + NG * kRows, kb1) - 1;
   // Smallest and largest key token of this wave (candidates are in token order).
-  const int wkmax = __builtin_amdgcn_readfirstlane(
-      (wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wlast) : -1);
-  const int wkmin = __builtin_amdgcn_readfirstlane(
-      (wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wc0) : 0x7fffffff);
+  const int wkmax = uni((wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wlast) : -1);
+  const int wkmin = uni((wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wc0) : 0x7fffffff);
 
   // Resident keys: group n, lane column lane % 32 is candidate wc0 + 32n + lane % 32.
   Chunk<DT> kf[NG][G::KCH];
@@ -441,20 +473,24 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
 
   const int tpt = kRows / F;  // tokens per streamed tile
   const int ntiles = (chunk_hi - row_lo + tpt - 1) / tpt;
-  const char *qbase = reinterpret_cast<const char *>(a.q);
+  // Query tile it: row r is (token row_lo + it*tpt + r/F, head h0 + r%F);
+  // rows of tokens from chunk_hi on are zero.
+  const char *qbase = reinterpret_cast<const char *>(a.q) + (long long)h0 * a.q_sh * G::ES;
+  const long long qtok_bytes = a.q_st * G::ES;
+  const int qhead_bytes = (int)(a.q_sh * G::ES);
+  auto tile_base = [&](int it) { return qbase + (long long)(row_lo + it * tpt) * qtok_bytes; };
+  auto tile_rows = [&](int it) { return (chunk_hi - (row_lo + it * tpt)) * F; };
+  // LSE of tile row r (threads 0..31), in log2 units; +inf for padding rows,
+  // which then contribute exp2(-inf) = 0.
   const long long T = a.L.T;
-  auto rowptr = [&](int it) {
-    return [=](int r) -> const char * {
-      const int t = row_lo + it * tpt + r / F;
-      if (t >= chunk_hi) return nullptr;
-      return qbase + ((long long)t * a.q_st + (long long)(h0 + r % F) * a.q_sh) * G::ES;
-    };
-  };
+  const float *lbase = a.lse_in + (long long)h0 * T;
+  const int loff = (int)(((threadIdx.x % F) * T + threadIdx.x / F) * 4);
   auto lse_load = [&](int it) -> float {
-    const int r = threadIdx.x;
-    const int t = row_lo + it * tpt + r / F;
-    if (t >= chunk_hi) return kPosInf;  // padding rows contribute exp2(-inf) = 0
-    return a.lse_in[(long long)(h0 + r % F) * T + t] * 1.44269504088896340736f;
+    const int nv = tile_rows(it);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(lbase + row_lo + it * tpt);
+    const float x = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x < nv ? loff : kOOB, 0, 0));
+    return (int)threadIdx.x < nv ? x * 1.44269504088896340736f : kPosInf;
   };
 
   float cs[NG];
@@ -462,13 +498,14 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   for (int n = 0; n < NG; ++n) cs[n] = 0.f;
 
   Stage<DT, D> st;
+  st.init([&](int r) { return (r / F) * (int)qtok_bytes + (r % F) * qhead_bytes; });
   float lreg = 0.f;
-  st.load(rowptr(0));
+  st.load(tile_base(0), tile_rows(0));
   if (threadIdx.x < kRows) lreg = lse_load(0);
   st.store(smem);
   if (threadIdx.x < kRows) reinterpret_cast<float *>(smem + G::TILE)[threadIdx.x] = lreg;
   if (ntiles > 1) {
-    st.load(rowptr(1));
+    st.load(tile_base(1), tile_rows(1));
     if (threadIdx.x < kRows) lreg = lse_load(1);
   }
   __syncthreads();
@@ -511,7 +548,7 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
       st.store(nb);
       if (threadIdx.x < kRows) reinterpret_cast<float *>(nb + G::TILE)[threadIdx.x] = lreg;
       if (it + 2 < ntiles) {
-        st.load(rowptr(it + 2));
+        st.load(tile_base(it + 2), tile_rows(it + 2));
         if (threadIdx.x < kRows) lreg = lse_load(it + 2);
       }
     }

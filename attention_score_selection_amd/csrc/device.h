@@ -12,6 +12,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// A value the caller knows to be the same in every lane, moved to a scalar
+// register.  Branches on such values then need no exec-mask bookkeeping.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = lane_id();

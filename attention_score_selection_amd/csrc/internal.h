@@ -89,6 +89,10 @@ hipError_t launch_gather(const void *emb, long long emb_stride, long long row_by
 
 constexpr int kCompactBlock = 1024;
 
+// Streamed tiles are read through buffer resources whose range ends here;
+// offsets at or past it read as zero.
+constexpr int kBufferLimit = 0x7FFFFFF0;
+
 // Resident 32-row groups per wave for a (dtype, head_dim): one group holds
 // (head_dim/16) x 8 values per lane; the total must leave room for the
 // accumulators within 256 VGPRs (two waves per SIMD).
