@@ -52,7 +52,10 @@ def build(verbose: bool = False) -> str:
         with ThreadPoolExecutor(len(SOURCES)) as ex:
             objs = list(ex.map(one, SOURCES))
         tmp_lib = os.path.join(tmp, "libtsel.so")
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        # --no-undefined: a kernel whose host stub went missing fails here,
+        # not at load time on the GPU.
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs,
+               "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

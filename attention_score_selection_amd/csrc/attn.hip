@@ -23,6 +23,12 @@
 // Query heads that share a KV head are folded into the row dimension (F heads
 // per token in each 32-row group), so one key fragment serves F query heads.
 //
+// Streamed tiles reach LDS through buffer loads whose per-lane offsets are
+// fixed for the whole job: the LSE pass stages through registers (one tile
+// ahead), the column-score pass uses the LDS-direct form of the buffer load
+// (no staging registers; measured faster there, while the LSE pass measured
+// slightly faster with register staging).
+//
 // A 16-wide k chunk is split over the two lane halves, 8 consecutive values
 // each (16 B for 16-bit types).  For fp32 the same 8 values feed eight 32x32x2
 // steps; A and B use the same permutation of k, so the contraction is
@@ -100,7 +106,11 @@ struct Geom {
   static constexpr int RS = ROW + 16;                  // LDS row stride (bank spread)
   static constexpr int UNITS = ROW / 16;               // 16-byte units per row
   static constexpr int UPT = (kRows * UNITS + 255) / 256;  // units per thread (256 threads)
-  static constexpr int TILE = kRows * RS;              // bytes of one tile
+  // LDS tile: 16-byte slots, UNITS + 1 per row (the last pads the row), the
+  // slot count rounded up to whole 64-slot blocks (one wave's direct load).
+  static constexpr int SLOTS_ROW = UNITS + 1;
+  static constexpr int NBLK = (kRows * SLOTS_ROW + 63) / 64;
+  static constexpr int TILE = NBLK * 64 * 16;          // bytes of one tile
 };
 
 // Buffer offset past every valid byte: a load there returns zero.  Host-side
@@ -109,8 +119,13 @@ constexpr int kOOB = kBufferLimit;
 
 // Buffer resource for raw (unstructured) loads from `base`; on gfx9 parts the
 // third word selects 32-bit data format so that offset range checking applies.
+// `base` must be wave-uniform; it is moved to scalar registers explicitly so
+// that the resource never needs a per-lane loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, kOOB, 0x00020000);
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  const unsigned long long u = (unsigned long long)(unsigned)uni((int)(p >> 32)) << 32 |
+                               (unsigned)uni((int)(unsigned)p);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), (short)0, kOOB, 0x00020000);
 }
 
 // Register staging of one streamed tile: global -> VGPR -> LDS.  Each thread
@@ -118,7 +133,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) 
 // tile's first row are computed once, so a step costs one compare and one
 // select per unit.  Units of rows past the valid range read as zero.
 template <int DT, int D>
-struct Stage {
+struct StageRegs {
   using G = Geom<DT, D>;
   uint4 r[G::UPT];
   int off[G::UPT];  // byte offset of unit i from the tile base
@@ -156,6 +171,59 @@ struct Stage {
         *reinterpret_cast<uint4 *>(tile + rr * G::RS + col * 16) = r[i];
       }
     }
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Staging of one streamed tile straight from global memory into LDS (buffer
+// loads with the LDS-direct option: lane l of a wave writes 16 bytes at the
+// block's LDS base + 16*l).  The tile's 64-slot blocks are dealt to the waves
+// round-robin; each lane's slot maps to a fixed (row, 16-byte unit), whose
+// byte offset from the tile base is computed once.  Padding slots, and rows
+// past the valid range, read as zero.
+template <int DT, int D>
+struct StageDirect {
+  using G = Geom<DT, D>;
+  static constexpr int BPW = (G::NBLK + 3) / 4;  // blocks per wave (at most)
+  int off[BPW];  // byte offset of this lane's unit in block 4*j + wave
+  int row[BPW];  // its tile row (kRows: padding or past the tile)
+
+  // rowoff(row): byte offset of tile row `row` from the tile base.
+  template <typename RowOff>
+  __device__ __forceinline__ void init(RowOff rowoff) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int slot = 64 * (4 * j + w) + lane_id();
+      const int r = slot / G::SLOTS_ROW, u = slot % G::SLOTS_ROW;
+      if (r < kRows && u < G::UNITS) {
+        row[j] = r;
+        off[j] = rowoff(r) + u * 16;
+      } else {
+        row[j] = kRows;
+        off[j] = kOOB;
+      }
+    }
+  }
+  // Start the copy of tile rows [0, nvalid) from `base` (wave-uniform) into
+  // `tile`; the rest of the tile reads as zero.  Complete once this wave's
+  // vector-memory counter drains (a __syncthreads() waits for that).
+  __device__ __forceinline__ void load(char *tile, const char *base, int nvalid) const {
+    // (The host pass of the compiler only sees the declaration: the LDS-direct
+    // builtin has no host form, and referencing it there would make the host
+    // side drop the kernels that use it.)
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base);
+    const int w = uni(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int blk = 4 * j + w;
+      if (blk < G::NBLK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void_t *)(tile + blk * 1024), 16, row[j] < nvalid ? off[j] : kOOB, 0, 0, 0);
+    }
+#endif
   }
 };
 
@@ -255,7 +323,7 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
 #pragma unroll
   for (int n = 0; n < NG; ++n) acc[n] = MAXMODE ? kNegInf : 0.0f;
 
-  Stage<DT, D> st;
+  StageRegs<DT, D> st;
   st.init([&](int r) { return r * (int)krow; });
   st.load(tile_base(t0), tile_rows(t0));
   st.store(smem);
@@ -472,7 +540,7 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   wait_vmem();
 
   const int tpt = kRows / F;  // tokens per streamed tile
-  const int ntiles = (chunk_hi - row_lo + tpt - 1) / tpt;
+  const int ntiles = uni((chunk_hi - row_lo + tpt - 1) / tpt);
   // Query tile it: row r is (token row_lo + it*tpt + r/F, head h0 + r%F);
   // rows of tokens from chunk_hi on are zero.
   const char *qbase = reinterpret_cast<const char *>(a.q) + (long long)h0 * a.q_sh * G::ES;
@@ -480,50 +548,59 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   const int qhead_bytes = (int)(a.q_sh * G::ES);
   auto tile_base = [&](int it) { return qbase + (long long)(row_lo + it * tpt) * qtok_bytes; };
   auto tile_rows = [&](int it) { return (chunk_hi - (row_lo + it * tpt)) * F; };
-  // LSE of tile row r (threads 0..31), in log2 units; +inf for padding rows,
-  // which then contribute exp2(-inf) = 0.
+  // LSE of tile row r (threads 0..31): fetched one step ahead, converted to
+  // log2 units when staged; padding rows get +inf and so contribute
+  // exp2(-inf) = 0.
   const long long T = a.L.T;
   const float *lbase = a.lse_in + (long long)h0 * T;
   const int loff = (int)(((threadIdx.x % F) * T + threadIdx.x / F) * 4);
-  auto lse_load = [&](int it) -> float {
-    const int nv = tile_rows(it);
+  auto lse_fetch = [&](int it) -> float {
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(lbase + row_lo + it * tpt);
-    const float x = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x < nv ? loff : kOOB, 0, 0));
-    return (int)threadIdx.x < nv ? x * 1.44269504088896340736f : kPosInf;
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x < tile_rows(it) ? loff : kOOB, 0, 0));
   };
-
   float cs[NG];
 #pragma unroll
   for (int n = 0; n < NG; ++n) cs[n] = 0.f;
 
-  Stage<DT, D> st;
+  StageDirect<DT, D> st;
   st.init([&](int r) { return (r / F) * (int)qtok_bytes + (r % F) * qhead_bytes; });
+  auto buf = [&](int it) { return smem + (it & 1) * BUF; };
+  auto stage_lse = [&](int it, float v) {
+    if (threadIdx.x < kRows)
+      reinterpret_cast<float *>(buf(it) + G::TILE)[threadIdx.x] =
+          (int)threadIdx.x < tile_rows(it) ? v * 1.44269504088896340736f : kPosInf;
+  };
   float lreg = 0.f;
-  st.load(tile_base(0), tile_rows(0));
-  if (threadIdx.x < kRows) lreg = lse_load(0);
-  st.store(smem);
-  if (threadIdx.x < kRows) reinterpret_cast<float *>(smem + G::TILE)[threadIdx.x] = lreg;
-  if (ntiles > 1) {
-    st.load(tile_base(1), tile_rows(1));
-    if (threadIdx.x < kRows) lreg = lse_load(1);
-  }
+  st.load(buf(0), tile_base(0), tile_rows(0));
+  if (threadIdx.x < kRows) lreg = lse_fetch(0);
+  stage_lse(0, lreg);
+  if (ntiles > 1 && threadIdx.x < kRows) lreg = lse_fetch(1);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
-    const char *buf = smem + (it & 1) * BUF;
+    const char *b = buf(it);
     const int tt0 = row_lo + it * tpt;
-    if (!(a.causal && tt0 + tpt - 1 < wkmin)) {  // otherwise every row precedes every key
-      Chunk<DT> af[G::KCH];
-      read_frag<DT, D>(af, buf);
+    const bool run = !(a.causal && tt0 + tpt - 1 < wkmin);  // otherwise every row precedes every key
+    Chunk<DT> af[G::KCH];
+    float l2[16];
+    if (run) {
+      read_frag<DT, D>(af, b);
       // LSE of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3.
-      float l2[16];
-      const float *lb = reinterpret_cast<const float *>(buf + G::TILE) + 4 * (lane >> 5);
+      const float *lb = reinterpret_cast<const float *>(b + G::TILE) + 4 * (lane >> 5);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
       }
+    }
+    // The other buffer was last read in the previous step: refill it now.
+    if (it + 1 < ntiles) {
+      st.load(buf(it + 1), tile_base(it + 1), tile_rows(it + 1));
+      stage_lse(it + 1, lreg);
+      if (it + 2 < ntiles && threadIdx.x < kRows) lreg = lse_fetch(it + 2);
+    }
+    if (run) {
       f32x16 s[NG];
       tile_mma<DT, D, NG>(af, kf, s);
       // Causal: a row sees a key only if the key's token is not later.
@@ -542,15 +619,6 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
       };
       if (a.causal && tt0 < wkmax) epi(std::true_type{});
       else epi(std::false_type{});
-    }
-    if (it + 1 < ntiles) {
-      char *nb = smem + ((it + 1) & 1) * BUF;
-      st.store(nb);
-      if (threadIdx.x < kRows) reinterpret_cast<float *>(nb + G::TILE)[threadIdx.x] = lreg;
-      if (it + 2 < ntiles) {
-        st.load(tile_base(it + 2), tile_rows(it + 2));
-        if (threadIdx.x < kRows) lreg = lse_load(it + 2);
-      }
     }
     __syncthreads();
   }
