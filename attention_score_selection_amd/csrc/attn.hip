@@ -276,8 +276,10 @@ __device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[D / 16],
   }
 }
 
-// Row of the 32x32 accumulator held in register v by this lane.
-__device__ __forceinline__ int acc_row(int v) { return 8 * (v >> 2) + 4 * (lane_id() >> 5) + (v & 3); }
+// Row of the 32x32 accumulator held in register v by this lane is
+// acc_row_c(v) + 4 * (lane / 32); acc_row_c is a compile-time constant, so a
+// mask test against a per-lane threshold costs one compare per register.
+__device__ __forceinline__ constexpr int acc_row_c(int v) { return 8 * (v >> 2) + (v & 3); }
 
 // Sum of 16 values as a balanced tree (shorter dependency chains, smaller
 // rounding growth than a running sum).
@@ -342,11 +344,15 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
+          // Key of register v is k0 + acc_row_c(v) + 4*(lane/32): visible while
+          // below key_hi and (causal) not past the row's token qtok[n].
+          const int lim = MASKED ? min(key_hi - 1, a.causal ? qtok[n] : key_hi - 1) -
+                                       (k0 + 4 * (lane_id() >> 5))
+                                 : 0;
           float p[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int key = k0 + acc_row(v);
-            const bool vis = !MASKED || (key < key_hi && (!a.causal || key <= qtok[n]));
+            const bool vis = !MASKED || acc_row_c(v) <= lim;
             if (MAXMODE) p[v] = vis ? s[n][v] : kNegInf;
             else p[v] = vis ? fast_exp2(fmaf(s[n][v], a.c1, -m[n])) : 0.0f;
           }
@@ -608,11 +614,15 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
+          // Row of register v has token tt0 + (acc_row_c(v) + 4*(lane/32)) / F;
+          // it sees key token ktok[n] iff acc_row_c(v) >= (ktok[n] - tt0)*F -
+          // 4*(lane/32) (the clamp keeps past-the-end columns invisible).
+          const int thr = MASKED ? min(ktok[n] - tt0, kRows) * F - 4 * (lane >> 5) : 0;
           float p[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             p[v] = fast_exp2(fmaf(s[n][v], a.c1, -l2[v]));
-            if (MASKED) p[v] = (ktok[n] <= tt0 + acc_row(v) / F) ? p[v] : 0.0f;
+            if (MASKED) p[v] = (acc_row_c(v) >= thr) ? p[v] : 0.0f;
           }
           cs[n] += tree16(p);
         }
@@ -631,26 +641,48 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
   }
 }
 
-// score[c] = (sum over head blocks and row chunks that see c, fixed order) / (Hq * n_b).
+// score[c] = (sum over head blocks and row chunks that see c) / (Hq * n_b).
+// A workgroup covers 32 columns; thread t sums head blocks t/32, t/32 + 8, ...
+// over their row chunks (four independent partial sums, so the loads overlap),
+// then the eight per-thread totals of a column are added in head-block-group
+// order.  The order is fixed, so the result is deterministic.
 __global__ __launch_bounds__(256) void colscore_finalize(AttnArgs a, float *score) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.N) return;
-  const DevLayout &L = a.L;
-  const int s = upper_index(L.cu_cands, 0, L.S, c);  // image holding c
-  const int b = upper_index(L.cu_images, 0, L.B, s);  // request holding image s
-  const int seg = (a.segkind == SEG_REQ) ? b : s;
-  int seg_lo, seg_hi;
-  seg_tokens(L, a.segkind, seg, seg_lo, seg_hi);
-  const int tok = L.img_start[s] + (c - L.cu_cands[s]);
-  const int nrc = (seg_hi - seg_lo + a.RC - 1) / a.RC;
-  const int rc0 = a.causal ? (tok - seg_lo) / a.RC : 0;
+  __shared__ float part[8][33];
+  const int cl = threadIdx.x & 31, hg = threadIdx.x >> 5;
+  const int c = blockIdx.x * 32 + cl;
   float sum = 0.f;
-  for (int hb = 0; hb < a.nhb; ++hb) {
-    const float *p = a.partial + (long long)hb * a.RCmax * a.N + c;
-    for (int rc = rc0; rc < nrc; ++rc) sum += p[(long long)rc * a.N];
+  int b = 0;
+  if (c < a.N) {
+    const DevLayout &L = a.L;
+    const int s = upper_index(L.cu_cands, 0, L.S, c);  // image holding c
+    b = upper_index(L.cu_images, 0, L.B, s);           // request holding image s
+    const int seg = (a.segkind == SEG_REQ) ? b : s;
+    int seg_lo, seg_hi;
+    seg_tokens(L, a.segkind, seg, seg_lo, seg_hi);
+    const int tok = L.img_start[s] + (c - L.cu_cands[s]);
+    const int nrc = (seg_hi - seg_lo + a.RC - 1) / a.RC;
+    const int rc0 = a.causal ? (tok - seg_lo) / a.RC : 0;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int hb = hg; hb < a.nhb; hb += 8) {
+      const float *p = a.partial + (long long)hb * a.RCmax * a.N + c;
+      int rc = rc0;
+      for (; rc + 4 <= nrc; rc += 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += p[(long long)(rc + j) * a.N];
+      }
+      for (; rc < nrc; ++rc) acc[0] += p[(long long)rc * a.N];
+    }
+    sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
-  const int n_b = L.cu_seqlens[b + 1] - L.cu_seqlens[b];
-  score[c] = sum / ((float)a.hq * (float)n_b);
+  part[hg][cl] = sum;
+  __syncthreads();
+  if (hg == 0 && c < a.N) {
+    float t = part[0][cl];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) t += part[j][cl];
+    const int n_b = a.L.cu_seqlens[b + 1] - a.L.cu_seqlens[b];
+    score[c] = t / ((float)a.hq * (float)n_b);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -727,7 +759,7 @@ hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, float *score, h
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colscore_finalize, dim3((a.N + 255) / 256), dim3(256), 0, s, a, score);
+  hipLaunchKernelGGL(colscore_finalize, dim3((a.N + 31) / 32), dim3(256), 0, s, a, score);
   return hipGetLastError();
 }
 
