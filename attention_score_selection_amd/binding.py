@@ -17,13 +17,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtsel.so")
 
 TSEL_OK, TSEL_EINVAL, TSEL_EUNSUPPORTED, TSEL_EWORKSPACE, TSEL_EHIP = 0, -1, -2, -3, -4
-TSEL_F32, TSEL_F16, TSEL_BF16 = 0, 1, 2
+TSEL_F32, TSEL_F16, TSEL_BF16, TSEL_FP8_E4M3 = 0, 1, 2, 3
 MASKS = {"full": 0, "causal": 1, "blockdiag": 2}
 TSEL_OP_LSE, TSEL_OP_COLSCORE, TSEL_OP_TOPK, TSEL_OP_COMPACT = 0, 1, 2, 3
 EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact",
            "tsel_workspace_size", "tsel_last_error", "tsel_version")
 
-_DTYPES = {torch.float32: TSEL_F32, torch.float16: TSEL_F16, torch.bfloat16: TSEL_BF16}
+_DTYPES = {torch.float32: TSEL_F32, torch.float16: TSEL_F16, torch.bfloat16: TSEL_BF16,
+           torch.float8_e4m3fn: TSEL_FP8_E4M3}
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
@@ -135,7 +136,8 @@ def make_attn(q: torch.Tensor, k: torch.Tensor, mask: str, softmax_scale: float 
     if q.dim() != 3 or k.dim() != 3 or q.stride(2) != 1 or k.stride(2) != 1:
         raise ValueError("q and k must be [T, H, d] with a contiguous last dimension")
     if q.dtype != k.dtype or q.dtype not in _DTYPES:
-        raise ValueError("q and k must share one dtype among float32, float16, bfloat16")
+        raise ValueError("q and k must share one dtype among float32, float16, bfloat16, "
+                         "float8_e4m3fn")
     a = CAttn()
     a.dtype = _DTYPES[q.dtype]
     a.num_heads_q, a.num_heads_kv, a.head_dim = q.shape[1], k.shape[1], q.shape[2]

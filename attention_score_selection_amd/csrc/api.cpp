@@ -24,7 +24,7 @@ int fail(int code, const char *fmt, ...) {
 
 void clear_error() { g_err.clear(); }
 
-static int elem_size(int dt) { return dt == TSEL_F32 ? 4 : 2; }
+static int elem_size(int dt) { return dt == TSEL_F32 ? 4 : dt == TSEL_FP8_E4M3 ? 1 : 2; }
 
 static int check_layout(const tsel_layout_t *l) {
   if (l == nullptr) return fail(TSEL_EINVAL, "layout is NULL");
@@ -61,10 +61,13 @@ static int check_layout(const tsel_layout_t *l) {
 
 static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
   if (a == nullptr) return fail(TSEL_EINVAL, "attn is NULL");
-  if (a->dtype != TSEL_F32 && a->dtype != TSEL_F16 && a->dtype != TSEL_BF16)
+  if (a->dtype != TSEL_F32 && a->dtype != TSEL_F16 && a->dtype != TSEL_BF16 &&
+      a->dtype != TSEL_FP8_E4M3)
     return fail(TSEL_EUNSUPPORTED, "dtype %d is not supported", (int)a->dtype);
   if (a->head_dim != 64 && a->head_dim != 80 && a->head_dim != 96 && a->head_dim != 128)
     return fail(TSEL_EUNSUPPORTED, "head_dim %d is not one of 64, 80, 96, 128", a->head_dim);
+  if (a->dtype == TSEL_FP8_E4M3 && a->head_dim != 64 && a->head_dim != 128)
+    return fail(TSEL_EUNSUPPORTED, "fp8 inputs need head_dim 64 or 128 (got %d)", a->head_dim);
   if (a->num_heads_q < 1 || a->num_heads_kv < 1 || a->num_heads_q % a->num_heads_kv != 0)
     return fail(TSEL_EINVAL, "num_heads_q (%d) must be a positive multiple of num_heads_kv (%d)",
                 a->num_heads_q, a->num_heads_kv);

@@ -44,26 +44,34 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int DT> struct Elem { static constexpr int ES = 2; };
-template <> struct Elem<TSEL_F32> { static constexpr int ES = 4; };
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// 8 consecutive k values of one row: 16 B (16-bit types) or 32 B (fp32).
+// Element size ES (bytes) and k width KW of one MFMA step per data type.
+// 16-bit types: one 32x32x16 MFMA per 16 k values; fp32: eight 32x32x2
+// MFMAs per 16 k values; fp8 (OCP E4M3): one 32x32x64 MFMA per 64 k values.
+template <int DT> struct Elem { static constexpr int ES = 2, KW = 16; };
+template <> struct Elem<TSEL_F32> { static constexpr int ES = 4, KW = 16; };
+template <> struct Elem<TSEL_FP8_E4M3> { static constexpr int ES = 1, KW = 64; };
+
+// This lane's share of one k chunk of one row: KW/2 consecutive k values
+// (16 B for 16-bit types, 32 B for fp32 and fp8).
 template <int DT>
 struct Chunk {
-  uint4 v[Elem<DT>::ES / 2];
+  static constexpr int NV = Elem<DT>::KW / 2 * Elem<DT>::ES / 16;
+  uint4 v[NV];
 };
 
 template <int DT>
 __device__ __forceinline__ void zero_chunk(Chunk<DT> &c) {
 #pragma unroll
-  for (int i = 0; i < Elem<DT>::ES / 2; ++i) c.v[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < Chunk<DT>::NV; ++i) c.v[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 template <int DT>
 __device__ __forceinline__ void load_chunk(Chunk<DT> &c, const char *p) {
   const uint4 *q = reinterpret_cast<const uint4 *>(p);
 #pragma unroll
-  for (int i = 0; i < Elem<DT>::ES / 2; ++i) c.v[i] = q[i];
+  for (int i = 0; i < Chunk<DT>::NV; ++i) c.v[i] = q[i];
 }
 
 template <int DT>
@@ -95,13 +103,26 @@ __device__ __forceinline__ f32x16 mma<TSEL_F32>(const Chunk<TSEL_F32> &a, const 
   return acc;
 }
 
+// fp8 E4M3 operands (format code 0 for both A and B), no block scaling.  A
+// and B fragments are loaded the same way (lane half h holds k values
+// 32h .. 32h+31 of the chunk), so the contraction pairs matching k.
+template <>
+__device__ __forceinline__ f32x16 mma<TSEL_FP8_E4M3>(const Chunk<TSEL_FP8_E4M3> &a,
+                                                     const Chunk<TSEL_FP8_E4M3> &b, f32x16 acc) {
+  struct P { uint4 x, y; };
+  const i32x8 av = __builtin_bit_cast(i32x8, P{a.v[0], a.v[1]});
+  const i32x8 bv = __builtin_bit_cast(i32x8, P{b.v[0], b.v[1]});
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+}
+
 constexpr int kRows = 32;  // rows of a streamed tile and of a resident group
 
 // Geometry of one streamed 32-row tile in LDS.
 template <int DT, int D>
 struct Geom {
   static constexpr int ES = Elem<DT>::ES;
-  static constexpr int KCH = D / 16;                   // 16-wide k chunks
+  static constexpr int KW = Elem<DT>::KW;
+  static constexpr int KCH = D / KW;                   // KW-wide k chunks (one MFMA step each)
   static constexpr int ROW = D * ES;                   // bytes of a row
   static constexpr int RS = ROW + 16;                  // LDS row stride (bank spread)
   static constexpr int UNITS = ROW / 16;               // 16-byte units per row
@@ -230,21 +251,17 @@ struct StageDirect {
 // This lane's fragment (row lane%32, k values 16*kc + 8*(lane/32) .. +8) of
 // an LDS tile.
 template <int DT, int D>
-__device__ __forceinline__ void read_frag(Chunk<DT> (&f)[D / 16], const char *tile) {
+__device__ __forceinline__ void read_frag(Chunk<DT> (&f)[D / Elem<DT>::KW], const char *tile) {
   using G = Geom<DT, D>;
   const int lane = lane_id();
-  const char *p = tile + (lane & 31) * G::RS + (lane >> 5) * 8 * G::ES;
+  const char *p = tile + (lane & 31) * G::RS + (lane >> 5) * (G::KW / 2) * G::ES;
 #pragma unroll
-  for (int kc = 0; kc < G::KCH; ++kc) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p + kc * 16 * G::ES);
-#pragma unroll
-    for (int i = 0; i < G::ES / 2; ++i) f[kc].v[i] = q[i];
-  }
+  for (int kc = 0; kc < G::KCH; ++kc) load_chunk<DT>(f[kc], p + kc * G::KW * G::ES);
 }
 
 // Load the resident fragments of NG 32-row groups straight from global memory.
 template <int DT, int D, int NG, typename RowPtr>
-__device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / 16], RowPtr rowptr) {
+__device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / Elem<DT>::KW], RowPtr rowptr) {
   using G = Geom<DT, D>;
   const int lane = lane_id();
 #pragma unroll
@@ -252,7 +269,7 @@ __device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / 16], RowP
     const char *p = rowptr(n * kRows + (lane & 31));
 #pragma unroll
     for (int kc = 0; kc < G::KCH; ++kc) {
-      const int e = 16 * kc + 8 * (lane >> 5);
+      const int e = G::KW * kc + (G::KW / 2) * (lane >> 5);
       if (p != nullptr) load_chunk<DT>(res[n][kc], p + e * G::ES);
       else zero_chunk<DT>(res[n][kc]);
     }
@@ -262,15 +279,16 @@ __device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / 16], RowP
 // acc[n] = A . R[n]^T for one streamed tile against all NG resident groups,
 // k chunks outermost so that the NG accumulation chains are independent.
 template <int DT, int D, int NG>
-__device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[D / 16],
-                                         const Chunk<DT> (&res)[NG][D / 16], f32x16 (&acc)[NG]) {
+__device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[D / Elem<DT>::KW],
+                                         const Chunk<DT> (&res)[NG][D / Elem<DT>::KW],
+                                         f32x16 (&acc)[NG]) {
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[n][v] = 0.f;
   }
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
+  for (int kc = 0; kc < D / Elem<DT>::KW; ++kc) {
 #pragma unroll
     for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[kc], res[n][kc], acc[n]);
   }
@@ -313,7 +331,8 @@ constexpr float kPosInf = __builtin_huge_valf();
 template <int DT, int D, int NG, bool MAXMODE>
 __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, int key_lo,
                                          int key_hi, int t0, int t1,
-                                         const Chunk<DT> (&qf)[NG][D / 16], const int (&qtok)[NG],
+                                         const Chunk<DT> (&qf)[NG][D / Elem<DT>::KW],
+                                         const int (&qtok)[NG],
                                          int wtok_min, int wtok_max, const float (&m)[NG],
                                          float (&acc)[NG]) {
   using G = Geom<DT, D>;
@@ -718,22 +737,32 @@ hipError_t col_ng(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   return col_go<DT, D, 1>(p, a, s);
 }
 
+// fp8 runs head_dim 64 and 128 only (whole 64-wide k chunks); the host
+// rejects the others before any launch.
 template <int DT>
 hipError_t lse_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
-  switch (p.D) {
-    case 64: return lse_ng<DT, 64>(p, a, s);
-    case 80: return lse_ng<DT, 80>(p, a, s);
-    case 96: return lse_ng<DT, 96>(p, a, s);
-    default: return lse_ng<DT, 128>(p, a, s);
+  if constexpr (DT == TSEL_FP8_E4M3) {
+    return p.D == 64 ? lse_ng<DT, 64>(p, a, s) : lse_ng<DT, 128>(p, a, s);
+  } else {
+    switch (p.D) {
+      case 64: return lse_ng<DT, 64>(p, a, s);
+      case 80: return lse_ng<DT, 80>(p, a, s);
+      case 96: return lse_ng<DT, 96>(p, a, s);
+      default: return lse_ng<DT, 128>(p, a, s);
+    }
   }
 }
 template <int DT>
 hipError_t col_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
-  switch (p.D) {
-    case 64: return col_ng<DT, 64>(p, a, s);
-    case 80: return col_ng<DT, 80>(p, a, s);
-    case 96: return col_ng<DT, 96>(p, a, s);
-    default: return col_ng<DT, 128>(p, a, s);
+  if constexpr (DT == TSEL_FP8_E4M3) {
+    return p.D == 64 ? col_ng<DT, 64>(p, a, s) : col_ng<DT, 128>(p, a, s);
+  } else {
+    switch (p.D) {
+      case 64: return col_ng<DT, 64>(p, a, s);
+      case 80: return col_ng<DT, 80>(p, a, s);
+      case 96: return col_ng<DT, 96>(p, a, s);
+      default: return col_ng<DT, 128>(p, a, s);
+    }
   }
 }
 
@@ -744,6 +773,7 @@ hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   switch (p.dtype) {
     case TSEL_F32: return lse_d<TSEL_F32>(p, a, s);
     case TSEL_F16: return lse_d<TSEL_F16>(p, a, s);
+    case TSEL_FP8_E4M3: return lse_d<TSEL_FP8_E4M3>(p, a, s);
     default: return lse_d<TSEL_BF16>(p, a, s);
   }
 }
@@ -755,6 +785,7 @@ hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, float *score, h
     switch (p.dtype) {
       case TSEL_F32: e = col_d<TSEL_F32>(p, a, s); break;
       case TSEL_F16: e = col_d<TSEL_F16>(p, a, s); break;
+      case TSEL_FP8_E4M3: e = col_d<TSEL_FP8_E4M3>(p, a, s); break;
       default: e = col_d<TSEL_BF16>(p, a, s); break;
     }
     if (e != hipSuccess) return e;

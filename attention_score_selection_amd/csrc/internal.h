@@ -94,10 +94,12 @@ constexpr int kCompactBlock = 1024;
 constexpr int kBufferLimit = 0x7FFFFFF0;
 
 // Resident 32-row groups per wave for a (dtype, head_dim): one group holds
-// (head_dim/16) x 8 values per lane; the total must leave room for the
-// accumulators within 256 VGPRs (two waves per SIMD).
+// head_dim values of 32 rows, i.e. head_dim * elem_size / 8 VGPRs per lane;
+// the total must leave room for the accumulators within 256 VGPRs (two waves
+// per SIMD).
 constexpr int max_groups(int dtype, int head_dim) {
-  const int per_group = (head_dim / 16) * (dtype == TSEL_F32 ? 4 : 2) * 2;  // VGPRs
+  const int es = dtype == TSEL_F32 ? 4 : dtype == TSEL_FP8_E4M3 ? 1 : 2;
+  const int per_group = head_dim * es / 8;  // VGPRs
   return per_group <= 20 ? 4 : per_group <= 32 ? 3 : per_group <= 48 ? 2 : 1;
 }
 

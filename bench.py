@@ -25,7 +25,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_TFLOPS = {"bf16": 2516.6,   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+               "fp8": 5033.2}    # dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 
@@ -105,6 +106,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
+    ap.add_argument("--dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="Q/K storage type of the workload (fp8: OCP E4M3 with per-tensor factors)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -119,7 +122,9 @@ def main():
     import attention_score_selection_amd as tsel
     from workloads import make_config
 
-    prob = make_config(4)
+    prob = make_config(4) if args.dtype == "bf16" else make_config(4, dtype=args.dtype)
+    scale = prob.softmax_scale if prob.softmax_scale is not None else 0.0
+    peak = PEAK_TFLOPS[args.dtype]
     dev = torch.device("cuda:0")
     lay = tsel.Layout.from_problem(prob, dev)
     q, k, emb = prob.q.to(dev), prob.k.to(dev), prob.emb.to(dev)
@@ -131,11 +136,12 @@ def main():
     lse = torch.empty((prob.hq, prob.T), dtype=torch.float32, device=dev)
     score = torch.empty((prob.N,), dtype=torch.float32, device=dev)
     keep = torch.empty((prob.N,), dtype=torch.uint8, device=dev)
-    ws_col = torch.empty((max(16, tsel.tsel_workspace_size(1, lay, q, k, prob.mask)),),
+    ws_col = torch.empty((max(16, tsel.tsel_workspace_size(1, lay, q, k, prob.mask, scale)),),
                          dtype=torch.uint8, device=dev)
     ws_cmp = torch.empty((tsel.tsel_workspace_size(3, lay),), dtype=torch.uint8, device=dev)
-    _, ks = tsel.tsel_budget_topk(lay, tsel.tsel_colscore(q, k, lay, prob.mask,
-                                                          tsel.tsel_lse(q, k, lay, prob.mask)), ratios)
+    _, ks = tsel.tsel_budget_topk(
+        lay, tsel.tsel_colscore(q, k, lay, prob.mask, tsel.tsel_lse(q, k, lay, prob.mask, scale), scale),
+        ratios)
     outs = {}
     tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
     t_out = int(outs["token_idx"].numel())
@@ -143,9 +149,9 @@ def main():
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        tsel.tsel_lse(q, k, lay, prob.mask, out=lse)
+        tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse)
         if ev: ev[1].record(stream)
-        tsel.tsel_colscore(q, k, lay, prob.mask, lse, out=score, workspace=ws_col)
+        tsel.tsel_colscore(q, k, lay, prob.mask, lse, scale, out=score, workspace=ws_col)
         if ev: ev[2].record(stream)
         tsel.tsel_budget_topk(lay, score, ratios, out=keep)
         if ev: ev[3].record(stream)
@@ -179,7 +185,10 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded normal Q/K, std 1/sqrt(d); normal embeddings)",
+        "dtype": args.dtype,
+        "data": "synthetic (seeded normal Q/K, std 1/sqrt(d)" +
+                (", quantised to fp8 E4M3 with per-tensor factors" if args.dtype == "fp8" else "") +
+                "; normal bf16 embeddings)",
         "config": {"workload": prob.name, "tokens": prob.T, "heads_q": prob.hq, "heads_kv": prob.hkv,
                    "head_dim": d, "mask": prob.mask, "vision_candidates": prob.N, "images": prob.S,
                    "keep_ratio": float(ratios[0]), "kept_vision": kept, "tokens_out": t_out,
@@ -187,14 +196,14 @@ def main():
         "phases_ms": {"lse": t_lse * 1e3, "colscore": t_col * 1e3, "budget_topk": t_topk * 1e3,
                       "compact_gather": t_cmp * 1e3},
         "colscore_elements_per_s": col_elems / t_col,
-        "colscore_mfma_frac": col_flops / t_col / 1e12 / PEAK_BF16_TFLOPS,
+        "colscore_mfma_frac": col_flops / t_col / 1e12 / peak,
         "lse_elements_per_s": lse_elems / t_lse,
-        "lse_mfma_frac": lse_flops / t_lse / 1e12 / PEAK_BF16_TFLOPS,
+        "lse_mfma_frac": lse_flops / t_lse / 1e12 / peak,
         "kept_tokens_per_s": kept / (t_topk + t_cmp),
         "select_gather_GBps": gather_bytes / (t_topk + t_cmp) / 1e9,
         "roofline": {"kernel": dominant[0], "bound": "mfma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak,
                      "traffic": stored_traffic(prob.name, dominant[0])},
     }
     if args.calib_copy_mb > 0:

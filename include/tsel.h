@@ -55,7 +55,12 @@ extern "C" {
 #define TSEL_EWORKSPACE (-3)  /* workspace missing or smaller than required        */
 #define TSEL_EHIP (-4)        /* a HIP launch reported an error                    */
 
-typedef enum { TSEL_F32 = 0, TSEL_F16 = 1, TSEL_BF16 = 2 } tsel_dtype_t;
+/* Q/K element types.  TSEL_FP8_E4M3 is the OCP 8-bit float with 4 exponent
+ * bits (bias 7), 3 mantissa bits, subnormals, no infinities and NaN =
+ * S.1111.111 (largest finite 448); the low-precision Q/K scoring LiteVLM
+ * deploys (LiteVLM review, sections 3.2 and 5).  Per-tensor dequantisation
+ * factors of q and k are folded into softmax_scale by the caller. */
+typedef enum { TSEL_F32 = 0, TSEL_F16 = 1, TSEL_BF16 = 2, TSEL_FP8_E4M3 = 3 } tsel_dtype_t;
 
 /* Which keys a row sees (the LiteVLM first decoder layer is causal; the
  * REDtech ViT-layer statistics use per-image bidirectional attention):
@@ -90,8 +95,9 @@ typedef struct {
 /* One attention layer's queries and keys.  q is [T, Hq, head_dim] and k is
  * [T, Hkv, head_dim] with arbitrary token and head strides (in ELEMENTS) and a
  * contiguous last dimension.  Query head h reads KV head h / (Hq / Hkv).
- * Requirements: Hq % Hkv == 0; head_dim in {64, 80, 96, 128}; q and k 16-byte
- * aligned; both strides multiples of 16 bytes.  softmax_scale <= 0 selects
+ * Requirements: Hq % Hkv == 0; head_dim in {64, 80, 96, 128} ({64, 128} for
+ * TSEL_FP8_E4M3); q and k 16-byte aligned; both strides multiples of 16
+ * bytes.  softmax_scale <= 0 selects
  * 1/sqrt(head_dim) (LiteVLM review, formula section). */
 typedef struct {
   tsel_dtype_t dtype;

@@ -47,15 +47,39 @@ import numpy as np
 ROW_BLOCK = 256
 
 
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Decode OCP FP8 E4M3 byte codes to float64, exactly: sign bit, 4
+    exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds
+    subnormals m * 2^-9; no infinities; exponent and mantissa all ones is
+    NaN (the format the LiteVLM review's FP8 deployment refers to)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sign * mag
+
+
 def to_f64(t) -> np.ndarray:
-    """Exact widening of stored fp32/f16/bf16 values to float64."""
+    """Exact widening of stored fp32/f16/bf16/fp8 values to float64."""
     try:
         import torch
         if isinstance(t, torch.Tensor):
-            return t.detach().to("cpu").to(torch.float64).numpy()
+            t = t.detach().to("cpu")
+            if t.dtype == torch.float8_e4m3fn:
+                return fp8_e4m3_to_f64(t.view(torch.uint8).numpy())
+            return t.to(torch.float64).numpy()
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(t, dtype=np.float64)
+
+
+def problem_scale(prob, d: int) -> float:
+    """The problem's softmax scale: its own (fp8 inputs carry dequantisation
+    factors) or 1/sqrt(d)."""
+    s = getattr(prob, "softmax_scale", None)
+    return default_scale(d) if s is None else float(s)
 
 
 def default_scale(d: int) -> float:
@@ -141,7 +165,7 @@ def attention_stats(prob, lse_in: Optional[np.ndarray] = None, scale: Optional[f
     hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
     assert hq % hkv == 0
     rep = hq // hkv
-    scale = default_scale(d) if scale is None else scale
+    scale = problem_scale(prob, d) if scale is None else scale
     causal = prob.mask == "causal"
     segs = attention_segments(prob)
     heads = list(range(hq)) if heads is None else list(heads)
@@ -175,7 +199,7 @@ def lse_rows(prob, tokens: Sequence[int], scale: Optional[float] = None) -> np.n
     q64, k64 = to_f64(prob.q), to_f64(prob.k)
     hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
     rep = hq // hkv
-    scale = default_scale(d) if scale is None else scale
+    scale = problem_scale(prob, d) if scale is None else scale
     segs = attention_segments(prob)
     out = np.full((hq, len(tokens)), np.nan)
     for col, t in enumerate(tokens):

@@ -2,8 +2,10 @@
 
 The oracle on that workload takes minutes of CPU time, too long for a GPU
 test, so its column masses are computed once here, by ``oracle/`` only, and
-stored with a digest of the regenerated Q/K bytes.  Run from the repository
-root:  python tests/golden/make_oracle_cache.py
+stored with a digest of the regenerated Q/K bytes (and the problem's softmax
+scale).  Run from the repository root:
+    python tests/golden/make_oracle_cache.py          # bf16 inputs -> oracle_c4.npz
+    python tests/golden/make_oracle_cache.py fp8      # fp8 inputs  -> oracle_c4_fp8.npz
 """
 import hashlib
 import os
@@ -28,11 +30,15 @@ def digest(prob) -> str:
 
 
 def main():
-    prob = make_config(4)
+    dtype = sys.argv[1] if len(sys.argv) > 1 else "bf16"
+    prob = make_config(4) if dtype == "bf16" else make_config(4, dtype=dtype)
     t0 = time.time()
     _, mass = oracle.attention_stats(prob, workers=oracle.default_workers())
-    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_c4.npz")
-    np.savez_compressed(out, mass=mass, digest=np.array(digest(prob)), name=np.array(prob.name))
+    fname = "oracle_c4.npz" if dtype == "bf16" else f"oracle_c4_{dtype}.npz"
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), fname)
+    scale = np.nan if prob.softmax_scale is None else prob.softmax_scale
+    np.savez_compressed(out, mass=mass, digest=np.array(digest(prob)), name=np.array(prob.name),
+                        scale=np.array(scale))
     print(f"wrote {out} in {time.time() - t0:.1f}s")
 
 

@@ -3,11 +3,14 @@
 Tolerances (written here, used by every GPU test):
 
 * scores: |gpu - oracle| <= max(rtol * |oracle|, 1e-6), rtol = 2e-3 for
-  bf16/f16 inputs and 1e-4 for fp32 inputs; the same rule is applied to the
+  bf16/f16/fp8 inputs and 1e-4 for fp32 inputs (fp8 inputs are the same
+  stored bits on both sides and their products are exact in the fp32
+  accumulator, so the fp32 pipeline after the dot product sets the error,
+  as for bf16); the same rule is applied to the
   column mass (score * Hq * n_b), whose magnitude is O(1), so the 1e-6 floor
   does not hide relative errors of tiny scores.
-* LSE: |gpu - oracle| <= 1e-4 (bf16/f16) or 1e-5 (fp32), absolute, natural
-  log units.
+* LSE: |gpu - oracle| <= 1e-4 (bf16/f16/fp8) or 1e-5 (fp32), absolute,
+  natural log units.
 * kept sets: exact, except inside the tie band of a pool: with oracle masses
   sorted descending and tau = max(rtol * m_(k), 1e-6), if m_(k) - m_(k+1) <=
   4 tau then the candidates with m_(k+1) - 2 tau <= m <= m_(k) + 2 tau may be
@@ -42,7 +45,8 @@ def run_gpu(prob, dev, lse=None, with_emb=True, emb=None):
     if with_emb:
         e = (prob.emb if emb is None else emb).to(dev)
     lse_t = None if lse is None else torch.as_tensor(lse, dtype=torch.float32).contiguous().to(dev)
-    out = tsel.select(q, k, lay, prob.mask, prob.keep_ratio, emb=e, lse=lse_t)
+    scale = prob.softmax_scale if prob.softmax_scale is not None else 0.0
+    out = tsel.select(q, k, lay, prob.mask, prob.keep_ratio, emb=e, lse=lse_t, softmax_scale=scale)
     torch.cuda.synchronize(dev)
     comp = {key: v.cpu() for key, v in out["compact"].items()}
     return dict(lse=out["lse"].cpu().double().numpy(), score=out["score"].cpu().double().numpy(),

@@ -107,6 +107,12 @@ def test_attn_validation_codes(lib):
     assert call_lse(lib, attn(mask=2), lay) == B.TSEL_EINVAL
     assert "BLOCKDIAG" in last_error(lib)
     assert lib.tsel_lse(None, ctypes.byref(lay.c), FAKE, None) == B.TSEL_EINVAL
+    # fp8 inputs take whole 64-wide k chunks only.
+    assert call_lse(lib, attn(dtype=B.TSEL_FP8_E4M3, d=96), lay) == B.TSEL_EUNSUPPORTED
+    assert "fp8" in last_error(lib)
+    # A 32-row tile must span less than 2 GiB of the buffers it is read from.
+    assert call_lse(lib, attn(st=(1 << 28, 128)), lay) == B.TSEL_EUNSUPPORTED
+    assert "2 GiB" in last_error(lib)
 
 
 @pytest.mark.parametrize("bad", ["cu_end", "overlap", "outside", "cands", "empty_grid", "no_reqs"])

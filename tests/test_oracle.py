@@ -62,14 +62,15 @@ def visible(prob, i, j):
     return True
 
 
-def mp_reference(prob):
-    """50-digit brute force: LSE per (h, i) and mass per candidate."""
+def mp_reference(prob, scale=None):
+    """50-digit brute force: LSE per (h, i) and mass per candidate.  Inputs are
+    widened by torch (its own fp8 decode included), not by the oracle."""
     mpmath.mp.dps = 50
-    q = O.to_f64(prob.q)
-    k = O.to_f64(prob.k)
+    q = prob.q.to(torch.float64).numpy()
+    k = prob.k.to(torch.float64).numpy()
     T, hq, d = q.shape
     rep = hq // k.shape[1]
-    scale = 1 / mpmath.sqrt(d)
+    scale = 1 / mpmath.sqrt(d) if scale is None else mpmath.mpf(scale)
     cand_tok = []
     for s in range(prob.S):
         n = int(prob.img_hw[s, 0] * prob.img_hw[s, 1])
@@ -109,6 +110,41 @@ def test_mpmath_bruteforce_tiny(mask):
     ref_lse, ref_mass = mp_reference(prob)
     for h in range(2):
         for i in range(T):
+            if ref_lse[h][i] is not None:
+                assert abs(lse[h, i] - float(ref_lse[h][i])) <= 1e-12 * max(1, abs(lse[h, i]))
+    for c in range(prob.N):
+        assert abs(mass[c] - float(ref_mass[c])) <= 1e-12 * max(1.0, float(ref_mass[c]))
+
+
+def test_fp8_decoder_matches_format():
+    """OCP E4M3: every byte code against torch's float8_e4m3fn widening, and
+    the format's landmarks (largest finite 448, smallest normal 2^-6, smallest
+    subnormal 2^-9, NaN codes, signed zero)."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine = O.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.array_equal(mine[~np.isnan(mine)], ref[~np.isnan(ref)])
+    assert mine[0x7E] == 448.0 and mine[0xFE] == -448.0
+    assert mine[0x08] == 2.0 ** -6 and mine[0x01] == 2.0 ** -9 and mine[0x07] == 7 * 2.0 ** -9
+    assert np.isnan(mine[0x7F]) and np.isnan(mine[0xFF]) and np.isnan(mine).sum() == 2
+    assert mine[0x80] == 0.0 and math.copysign(1.0, mine[0x80]) == -1.0
+    assert mine[0x38] == 1.0 and mine[0x3C] == 1.5
+
+
+@pytest.mark.parametrize("mask", ["full", "causal"])
+def test_fp8_problem_against_bruteforce(mask):
+    """An fp8 problem from the generator (per-tensor factors folded into its
+    softmax scale): the oracle's LSE and mass against 50-digit brute force
+    with that scale."""
+    reqs = [(6, [(1, 1, 3)]), (4, [(0, 2, 1)])]
+    prob = make_problem("fp8_tiny", reqs, 2, 1, 4, "fp8", mask, 1.0, 21, ratios=0.5, emb_dim=4)
+    assert prob.q.dtype == torch.float8_e4m3fn and prob.softmax_scale is not None
+    assert float(prob.q.to(torch.float32).abs().max()) == 448.0
+    lse, mass = oracle.attention_stats(prob)
+    ref_lse, ref_mass = mp_reference(prob, scale=prob.softmax_scale)
+    for h in range(2):
+        for i in range(prob.T):
             if ref_lse[h][i] is not None:
                 assert abs(lse[h, i] - float(ref_lse[h][i])) <= 1e-12 * max(1, abs(lse[h, i]))
     for c in range(prob.N):

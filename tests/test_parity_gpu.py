@@ -68,6 +68,37 @@ def test_medium_random(dev, i):
                  prob.emb)
 
 
+SMALL_FP8 = [("full", 4, 4, 64), ("causal", 8, 2, 128), ("blockdiag", 4, 2, 64), ("causal", 16, 1, 128)]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL_FP8)))
+def test_small_random_fp8(dev, i):
+    """OCP E4M3 inputs with per-tensor factors folded into the softmax scale."""
+    mask, hq, hkv, d = SMALL_FP8[i]
+    prob = random_small(150 + i, mask, dtype="fp8", hq=hq, hkv=hkv, d=d, n_req=3)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
+@pytest.mark.parametrize("mask,hq,hkv,d,std", [("causal", 8, 2, 128, 1.0), ("full", 16, 4, 64, 1.0),
+                                               ("causal", 64, 8, 128, 0.0884)])
+def test_medium_random_fp8(dev, mask, hq, hkv, d, std):
+    prob = random_medium(250 + hq, mask, dtype="fp8", hq=hq, hkv=hkv, d=d, n_req=2, std=std)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, workers=oracle.default_workers(), with_emb=False),
+                 prob.emb)
+
+
+def test_litevlm_workload_fp8(dev):
+    prob = make_config(2, dtype="fp8")
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, workers=oracle.default_workers(), with_emb=False),
+                 prob.emb)
+
+
 @pytest.mark.parametrize("cfg,std", [(1, None), (2, None), (2, 1.0), (3, None)])
 def test_named_workload_live_oracle(dev, cfg, std):
     prob = make_config(cfg, seed=cfg if std is None else cfg + 100, std=std)
@@ -96,6 +127,28 @@ def test_decoder_16384_gqa_full_size(dev):
     rows = np.linspace(0, prob.T - 1, 24).astype(int)
     ref_lse = oracle.lse_rows(prob, rows)
     P.check_lse(prob, got["lse"][:, rows], ref_lse)
+
+
+def test_decoder_16384_gqa_fp8_full_size(dev):
+    """The same layer with fp8 Q/K (the configuration the fp8 benchmark line
+    times): every score against stored oracle masses, kept set, compaction,
+    live LSE samples."""
+    cache = np.load(os.path.join(GOLDEN, "oracle_c4_fp8.npz"))
+    prob = make_config(4, dtype="fp8")
+    announce(prob)
+    assert input_digest(prob) == str(cache["digest"]), "regenerated inputs differ from the stored oracle's"
+    assert float(cache["scale"]) == prob.softmax_scale
+    got = P.run_gpu(prob, dev)
+    ref_mass = cache["mass"]
+    P.check_scores(prob, got["score"], ref_mass)
+    ref_keep, ref_k = oracle.topk(prob, oracle.scores(prob, ref_mass))
+    assert np.array_equal(got["k"], ref_k)
+    exact = P.check_keep(prob, got["keep"], ref_mass, ref_k)
+    P.check_compaction_valid(prob, got["keep"], got["compact"], prob.emb)
+    if exact:
+        P.check_compaction_exact(prob, got["compact"], oracle.compact(prob, ref_keep), prob.emb)
+    rows = np.linspace(0, prob.T - 1, 24).astype(int)
+    P.check_lse(prob, got["lse"][:, rows], oracle.lse_rows(prob, rows))
 
 
 def input_digest(prob):

@@ -20,7 +20,11 @@ the rows are only needed by the compaction checks and the benchmark.
 
 Q/K/emb are generated in fp32 and then rounded to the storage dtype with
 round-to-nearest-even (torch ``.to``), so every consumer reads the same
-stored bits.
+stored bits.  For fp8 (OCP E4M3) Q and K are first divided by a per-tensor
+factor (largest magnitude / 448, rounded to fp32) so that they span the
+format's range, and the problem's ``softmax_scale`` becomes
+``fp32(sq * sk / sqrt(d))``: the quantised logits then equal the original
+ones up to the fp8 rounding.  Embeddings of an fp8 problem are bf16.
 
 The five named workloads follow the problem statements of the pages: one
 ViT-layer image (LiteVLM / VisionZip single image), a LiteVLM-style
@@ -40,7 +44,9 @@ import numpy as np
 import torch
 
 MASKS = ("full", "causal", "blockdiag")
-DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "fp8": torch.float8_e4m3fn}
+FP8_MAX = 448.0
 
 
 @dataclass
@@ -71,6 +77,7 @@ class Problem:
     dtype: str = "bf16"
     std: float = 1.0
     dominant: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
+    softmax_scale: Optional[float] = None   # None: 1/sqrt(d)
     _emb: Optional[torch.Tensor] = None
 
     @property
@@ -149,6 +156,14 @@ def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DTYPES[dtype])
 
 
+def _quantize_fp8(x: np.ndarray):
+    """fp8 E4M3 copy of ``x`` divided by its per-tensor factor; returns
+    (tensor, factor)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    f = np.float32(amax / FP8_MAX) if amax > 0 else np.float32(1.0)
+    return _round(x / f, "fp8"), float(f)
+
+
 def make_problem(name: str, requests, hq: int, hkv: int, d: int, dtype: str, mask: str,
                  std: float, seed: int, ratios=None, ratio_range=None, emb_dim: int = 64,
                  emb_dtype: Optional[str] = None, dominant_spec=None,
@@ -189,11 +204,19 @@ def make_problem(name: str, requests, hq: int, hkv: int, d: int, dtype: str, mas
     else:
         lo, hi = ratio_range
         keep_ratio = rng.uniform(lo, hi, size=B)
-    return Problem(name=name, q=_round(qf, dtype), k=_round(kf, dtype), mask=mask,
+    softmax_scale = None
+    if dtype == "fp8":
+        q, fq = _quantize_fp8(qf)
+        k, fk = _quantize_fp8(kf)
+        softmax_scale = float(np.float32(fq * fk / np.sqrt(d)))
+        emb_dtype = emb_dtype or "bf16"
+    else:
+        q, k = _round(qf, dtype), _round(kf, dtype)
+    return Problem(name=name, q=q, k=k, mask=mask,
                    cu_seqlens=cu_seqlens, cu_images=cu_images, img_start=img_start,
                    img_hw=img_hw, cu_cands=cu_cands, keep_ratio=keep_ratio, emb_dim=emb_dim,
                    emb_dtype=emb_dtype or dtype, lse_supplied=lse_supplied, seed=seed,
-                   dtype=dtype, std=std, dominant=dom)
+                   dtype=dtype, std=std, dominant=dom, softmax_scale=softmax_scale)
 
 
 # ----------------------------------------------------------------------------
@@ -232,12 +255,19 @@ def varlen_layout(rng: np.random.Generator, n_req: int = 8, lmin: int = 2048, lm
     return reqs
 
 
-def make_config(cfg: int, seed: Optional[int] = None, std: Optional[float] = None) -> Problem:
+def make_config(cfg: int, seed: Optional[int] = None, std: Optional[float] = None,
+                dtype: Optional[str] = None) -> Problem:
     """Named workload ``cfg`` in 1..5 (seed defaults to ``cfg``).  ``std``
     overrides the Q/K standard deviation (used for the value-sensitive
-    variants of the near-uniform decoder workloads)."""
+    variants of the near-uniform decoder workloads).  ``dtype`` overrides the
+    Q/K storage type of the decoder workloads (2 and 4), e.g. "fp8" for the
+    low-precision scoring LiteVLM deploys; the name then says so."""
     seed = cfg if seed is None else seed
     name = CONFIG_NAMES[cfg]
+    if dtype is not None:
+        if cfg not in (2, 4):
+            raise ValueError("dtype override is defined for workloads 2 and 4")
+        name = name.replace("_bf16_", f"_{dtype}_")
     if cfg == 1:
         return make_problem(name, [(256, [(0, 16, 16)])], 4, 4, 64, "f32", "full",
                             1.0 if std is None else std, seed, ratios=0.4, emb_dim=256,
@@ -245,9 +275,9 @@ def make_config(cfg: int, seed: Optional[int] = None, std: Optional[float] = Non
     if cfg == 2:
         d = 128
         imgs = [(i * 256, 16, 16) for i in range(12)]
-        return make_problem(name, [(12 * 256 + 142, imgs)], 16, 16, d, "bf16", "causal",
+        return make_problem(name, [(12 * 256 + 142, imgs)], 16, 16, d, dtype or "bf16", "causal",
                             1.0 / np.sqrt(d) if std is None else std, seed, ratios=0.8,
-                            emb_dim=2048)
+                            emb_dim=2048, emb_dtype="bf16")
     if cfg == 3:
         imgs = [(i * 1024, 32, 32) for i in range(30)]
         return make_problem(name, [(30 * 1024, imgs)], 16, 16, 80, "bf16", "blockdiag",
@@ -256,9 +286,9 @@ def make_config(cfg: int, seed: Optional[int] = None, std: Optional[float] = Non
     if cfg == 4:
         d = 128
         imgs = [(i * 750, 25, 30) for i in range(20)]
-        return make_problem(name, [(16384, imgs)], 64, 8, d, "bf16", "causal",
+        return make_problem(name, [(16384, imgs)], 64, 8, d, dtype or "bf16", "causal",
                             1.0 / np.sqrt(d) if std is None else std, seed, ratios=0.6,
-                            emb_dim=5120)
+                            emb_dim=5120, emb_dtype="bf16")
     if cfg == 5:
         d = 128
         rng = np.random.default_rng(seed)
