@@ -556,6 +556,14 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
     const int c = wc0 + n * kRows + (lane & 31);
     ktok[n] = (c < kb1) ? cand_token(a.L, s_lo, s_hi, c) : 0x7fffffff;
   }
+  // Largest key token of each group (its last candidate before kb1; INT_MAX
+  // marks an empty group, which then always takes the masked path).
+  int gkmax[NG];
+#pragma unroll
+  for (int n = 0; n < NG; ++n) {
+    const int last = min(kRows - 1, kb1 - 1 - (wc0 + n * kRows));
+    gkmax[n] = last >= 0 ? uni(__shfl(ktok[n], last, 64)) : 0x7fffffff;
+  }
   const char *kbase = reinterpret_cast<const char *>(a.k);
   load_resident<DT, D, NG>(kf, [&](int j) -> const char * {
     const int t = ktok[j / kRows];
@@ -629,25 +637,32 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
       f32x16 s[NG];
       tile_mma<DT, D, NG>(af, kf, s);
       // Causal: a row sees a key only if the key's token is not later.
-      auto epi = [&](auto masked) {
+      auto epi = [&](int n, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
+        // Row of register v has token tt0 + (acc_row_c(v) + 4*(lane/32)) / F;
+        // it sees key token ktok[n] iff acc_row_c(v) >= (ktok[n] - tt0)*F -
+        // 4*(lane/32) (the clamp keeps past-the-end columns invisible).
+        const int thr = MASKED ? min(ktok[n] - tt0, kRows) * F - 4 * (lane >> 5) : 0;
+        float p[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          p[v] = fast_exp2(fmaf(s[n][v], a.c1, -l2[v]));
+          if (MASKED) p[v] = (acc_row_c(v) >= thr) ? p[v] : 0.0f;
+        }
+        cs[n] += tree16(p);
+      };
+      if (!a.causal || tt0 >= wkmax) {
+#pragma unroll
+        for (int n = 0; n < NG; ++n) epi(n, std::false_type{});
+      } else {
+        // Near the diagonal only the groups whose last key is later than the
+        // tile's first token need the mask.
 #pragma unroll
         for (int n = 0; n < NG; ++n) {
-          // Row of register v has token tt0 + (acc_row_c(v) + 4*(lane/32)) / F;
-          // it sees key token ktok[n] iff acc_row_c(v) >= (ktok[n] - tt0)*F -
-          // 4*(lane/32) (the clamp keeps past-the-end columns invisible).
-          const int thr = MASKED ? min(ktok[n] - tt0, kRows) * F - 4 * (lane >> 5) : 0;
-          float p[16];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            p[v] = fast_exp2(fmaf(s[n][v], a.c1, -l2[v]));
-            if (MASKED) p[v] = (acc_row_c(v) >= thr) ? p[v] : 0.0f;
-          }
-          cs[n] += tree16(p);
+          if (tt0 < gkmax[n]) epi(n, std::true_type{});
+          else epi(n, std::false_type{});
         }
-      };
-      if (a.causal && tt0 < wkmax) epi(std::true_type{});
-      else epi(std::false_type{});
+      }
     }
     __syncthreads();
   }
