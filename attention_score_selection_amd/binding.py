@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libtsel.so")
 TSEL_OK, TSEL_EINVAL, TSEL_EUNSUPPORTED, TSEL_EWORKSPACE, TSEL_EHIP = 0, -1, -2, -3, -4
 TSEL_F32, TSEL_F16, TSEL_BF16, TSEL_FP8_E4M3 = 0, 1, 2, 3
 MASKS = {"full": 0, "causal": 1, "blockdiag": 2}
-TSEL_OP_LSE, TSEL_OP_COLSCORE, TSEL_OP_TOPK, TSEL_OP_COMPACT = 0, 1, 2, 3
-EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact",
+TSEL_OP_LSE, TSEL_OP_COLSCORE, TSEL_OP_TOPK, TSEL_OP_COMPACT, TSEL_OP_MROPE = 0, 1, 2, 3, 4
+EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact", "tsel_mrope_positions",
            "tsel_workspace_size", "tsel_last_error", "tsel_version")
 
 _DTYPES = {torch.float32: TSEL_F32, torch.float16: TSEL_F16, torch.bfloat16: TSEL_BF16,
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.tsel_compact.argtypes = [ctypes.POINTER(CLayout), _P, _P, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]
+        L.tsel_mrope_positions.restype = ctypes.c_int
+        L.tsel_mrope_positions.argtypes = [ctypes.POINTER(CLayout), _P, _P, ctypes.c_int32, _P, _P,
+                                           ctypes.c_size_t, _P]
         _lib = L
     return _lib
 
@@ -232,13 +235,33 @@ def tsel_compact(layout: Layout, keep: torch.Tensor, k_per_pool, emb: Optional[t
     return o
 
 
+def tsel_mrope_positions(layout: Layout, compact: dict, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rotary (t, h, w) positions [T_out, 3] of the compacted sequence, from
+    tsel_compact's token_idx and spatial outputs."""
+    tok, sp = compact["token_idx"], compact["spatial"]
+    dev = tok.device
+    n = int(tok.numel())
+    if out is None:
+        out = torch.empty((n, 3), dtype=torch.int32, device=dev)
+    need = tsel_workspace_size(TSEL_OP_MROPE, layout)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty((max(need, 4),), dtype=torch.uint8, device=dev)
+    _check(lib().tsel_mrope_positions(ctypes.byref(layout.c), _ptr(tok), _ptr(sp), n, _ptr(out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(dev)))
+    return out
+
+
 def select(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask: str, keep_ratio,
            emb: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
            softmax_scale: float = 0.0) -> dict:
-    """The whole path: LSE (unless supplied) -> scores -> budget top-k -> compaction."""
+    """The whole path: LSE (unless supplied) -> scores -> budget top-k -> compaction
+    -> rotary positions of the compacted sequence."""
     if lse is None:
         lse = tsel_lse(q, k, layout, mask, softmax_scale)
     score = tsel_colscore(q, k, layout, mask, lse, softmax_scale)
     keep, ks = tsel_budget_topk(layout, score, keep_ratio)
     comp = tsel_compact(layout, keep, ks, emb)
+    comp["positions"] = tsel_mrope_positions(layout, comp)
     return dict(lse=lse, score=score, keep=keep, k=ks, compact=comp)

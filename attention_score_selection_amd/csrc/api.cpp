@@ -265,6 +265,8 @@ size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t 
       return 0;
     case TSEL_OP_COMPACT:
       return compact_ws(layout);
+    case TSEL_OP_MROPE:
+      return (size_t)layout->num_images * sizeof(int32_t);
     default:
       fail(TSEL_EINVAL, "unknown op %d", op);
       return (size_t)-1;
@@ -382,6 +384,26 @@ int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *e
     e = launch_gather(emb, emb_stride, emb_row_bytes, out_emb, out_emb_stride, out_token_idx, c.total,
                       out_capacity, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_compact launch: %s", hipGetErrorString(e));
+  return TSEL_OK;
+}
+
+int tsel_mrope_positions(const tsel_layout_t *layout, const int32_t *out_token_idx,
+                         const int32_t *out_spatial, int32_t n_out, int32_t *out_pos,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc != TSEL_OK) return rc;
+  if (n_out < 0) return fail(TSEL_EINVAL, "n_out must be >= 0");
+  if (n_out > 0 && (out_token_idx == nullptr || out_spatial == nullptr || out_pos == nullptr))
+    return fail(TSEL_EINVAL, "out_token_idx, out_spatial and out_pos are required");
+  const size_t need = (size_t)layout->num_images * sizeof(int32_t);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(TSEL_EWORKSPACE, "tsel_mrope_positions needs %zu workspace bytes (got %zu)", need,
+                workspace_bytes);
+  if ((uintptr_t)workspace & 3) return fail(TSEL_EINVAL, "workspace must be 4-byte aligned");
+  hipError_t e = launch_mrope(dev_layout(layout), reinterpret_cast<int *>(workspace), out_token_idx,
+                              out_spatial, n_out, out_pos, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_mrope_positions launch: %s", hipGetErrorString(e));
   return TSEL_OK;
 }
 

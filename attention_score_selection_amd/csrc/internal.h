@@ -87,6 +87,9 @@ hipError_t launch_gather(const void *emb, long long emb_stride, long long row_by
                          long long out_stride, const int *token_idx, const int *total, int cap,
                          hipStream_t s);
 
+hipError_t launch_mrope(const DevLayout &L, int *adj, const int *tok, const int *sp, int n, int *pos,
+                        hipStream_t s);
+
 constexpr int kCompactBlock = 1024;
 
 // Streamed tiles are read through buffer resources whose range ends here;

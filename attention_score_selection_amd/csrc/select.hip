@@ -224,7 +224,64 @@ __global__ __launch_bounds__(256) void gather_rows(const char *emb, long long em
   }
 }
 
+// mRoPE positions of the compacted sequence.  Running index of a request:
+// text tokens advance it by 1, an image of rows x cols by max(rows, cols);
+// adj[s] is what the images of s's request before s add on top of their
+// token counts (sum of max(rows, cols) - rows*cols), one thread per request.
+__global__ __launch_bounds__(256) void mrope_image_adjust(DevLayout L, int *adj) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= L.B) return;
+  int acc = 0;
+  for (int s = L.cu_images[b]; s < L.cu_images[b + 1]; ++s) {
+    adj[s] = acc;
+    const int gh = L.img_hw[2 * s], gw = L.img_hw[2 * s + 1];
+    acc += max(gh, gw) - gh * gw;
+  }
+}
+
+// One thread per output row p: (i, i, i) for a text token whose running index
+// is i; (i0, i0 + row, i0 + col) for an image token, i0 being the index at
+// its image's first token.  Rows whose token index is out of range get -1.
+__global__ __launch_bounds__(256) void mrope_positions(DevLayout L, const int *adj, const int *tok,
+                                                       const int *sp, int n, int *pos) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= n) return;
+  const int t = tok[p];
+  int x = -1, y = -1, z = -1;
+  if (t >= 0 && t < L.T) {
+    const int b = upper_index(L.cu_seqlens, 0, L.B, t);
+    const int lo = L.cu_seqlens[b];
+    const int s = sp[3 * p];
+    if (s >= 0 && s < L.S) {
+      const int i0 = L.img_start[s] - lo + adj[s];
+      x = i0;
+      y = i0 + sp[3 * p + 1];
+      z = i0 + sp[3 * p + 2];
+    } else {
+      const int j = upper_index(L.img_start, L.cu_images[b], L.cu_images[b + 1], t);
+      int i = t - lo;
+      if (j >= L.cu_images[b]) {
+        const int gh = L.img_hw[2 * j], gw = L.img_hw[2 * j + 1];
+        i += adj[j] + max(gh, gw) - gh * gw;
+      }
+      x = y = z = i;
+    }
+  }
+  pos[3 * p] = x;
+  pos[3 * p + 1] = y;
+  pos[3 * p + 2] = z;
+}
+
 }  // namespace
+
+hipError_t launch_mrope(const DevLayout &L, int *adj, const int *tok, const int *sp, int n, int *pos,
+                        hipStream_t s) {
+  if (L.B > 0 && L.S > 0)
+    hipLaunchKernelGGL(mrope_image_adjust, dim3((L.B + 255) / 256), dim3(256), 0, s, L, adj);
+  if (n > 0)
+    hipLaunchKernelGGL(mrope_positions, dim3((n + 255) / 256), dim3(256), 0, s, L, adj, tok, sp, n, pos);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const DevLayout &L, const float *score, const TopkChunk &ks, int npools,
                        uint8_t *keep, hipStream_t s) {

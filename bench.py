@@ -2,7 +2,8 @@
 
 One step = the whole path over one batch already resident in HBM:
 tsel_lse -> tsel_colscore -> tsel_budget_topk -> tsel_compact (with the
-embedding-row gather), on the 16384-token GQA decoder-layer workload
+embedding-row gather) -> tsel_mrope_positions, on the 16384-token GQA
+decoder-layer workload
 (64 query heads / 8 KV heads, head_dim 128, bf16, causal, 15000 vision
 tokens in 20 images of 25x30 plus 1384 text tokens, keep 60%, 5120-dim bf16
 hidden states gathered).
@@ -145,6 +146,8 @@ def main():
     outs = {}
     tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
     t_out = int(outs["token_idx"].numel())
+    pos = torch.empty((t_out, 3), dtype=torch.int32, device=dev)
+    ws_rope = torch.empty((max(4, tsel.tsel_workspace_size(4, lay)),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -157,18 +160,20 @@ def main():
         if ev: ev[3].record(stream)
         tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
         if ev: ev[4].record(stream)
+        tsel.tsel_mrope_positions(lay, outs, out=pos, workspace=ws_rope)
+        if ev: ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events]) / 1e3
-    t_lse, t_col, t_topk, t_cmp = phase.mean(axis=0)
+    phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in events]) / 1e3
+    t_lse, t_col, t_topk, t_cmp, t_rope = phase.mean(axis=0)
     ms_per_step = wall / args.steps * 1e3
 
     col_flops = 2.0 * d * col_elems
@@ -194,7 +199,7 @@ def main():
                    "keep_ratio": float(ratios[0]), "kept_vision": kept, "tokens_out": t_out,
                    "emb_dim": prob.emb_dim, "lse": "computed in-library"},
         "phases_ms": {"lse": t_lse * 1e3, "colscore": t_col * 1e3, "budget_topk": t_topk * 1e3,
-                      "compact_gather": t_cmp * 1e3},
+                      "compact_gather": t_cmp * 1e3, "rope_positions": t_rope * 1e3},
         "colscore_elements_per_s": col_elems / t_col,
         "colscore_mfma_frac": col_flops / t_col / 1e12 / peak,
         "lse_elements_per_s": lse_elems / t_lse,

@@ -117,9 +117,11 @@ typedef struct {
 #define TSEL_OP_COLSCORE 1
 #define TSEL_OP_TOPK 2
 #define TSEL_OP_COMPACT 3
+#define TSEL_OP_MROPE 4
 
 /* Bytes of workspace `op` needs for this problem (0 if none; the caller may
- * then pass NULL).  `attn` may be NULL for TSEL_OP_TOPK / TSEL_OP_COMPACT.
+ * then pass NULL).  `attn` may be NULL for TSEL_OP_TOPK / TSEL_OP_COMPACT /
+ * TSEL_OP_MROPE.
  * Returns (size_t)-1 when the arguments fail validation. */
 size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t *layout);
 
@@ -173,6 +175,25 @@ int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *e
                  int64_t out_emb_stride, int32_t *out_token_idx, int32_t *out_spatial,
                  int32_t *out_cu_seqlens, int32_t *out_img_counts, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/* Rotary position ids of the compacted sequence, for a prefill that takes it
+ * (REDtech article, section 3.2: the mRoPE positions are updated together
+ * with lengths, image boundaries and spatial indices so the shorter sequence
+ * enters prefill unchanged otherwise).  The pages name the update but not the
+ * rule; the reading taken is that every kept token keeps the position it had
+ * in its full request under the multimodal rotary scheme of the Qwen-VL
+ * models the article serves: a running index starts at 0 in every request,
+ * a text token gets (i, i, i) and advances it by 1, an image of rows x cols
+ * whose first token meets index i gives token (row, col) the position
+ * (i, i + row, i + col) and advances the index by max(rows, cols).
+ *   out_token_idx, out_spatial: tsel_compact's outputs for this layout (the
+ *                  first n_out rows are read);
+ *   out_pos        int32 [n_out, 3] (t, h, w); a row whose token index is
+ *                  outside [0, T) gets (-1, -1, -1).
+ * Workspace: tsel_workspace_size(TSEL_OP_MROPE) bytes (one int32 per image). */
+int tsel_mrope_positions(const tsel_layout_t *layout, const int32_t *out_token_idx,
+                         const int32_t *out_spatial, int32_t n_out, int32_t *out_pos,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Description of the last error on this thread ("" if none). */
 const char *tsel_last_error(void);

@@ -301,7 +301,39 @@ def compact(prob, keep: np.ndarray, emb=None):
                cu_seqlens=cu_out.astype(np.int64), img_counts=img_counts)
     if emb is not None:
         out["emb"] = emb[token_idx]
+    out["positions"] = rope_positions(prob)[token_idx]
     return out
+
+
+def rope_positions(prob) -> np.ndarray:
+    """Rotary (t, h, w) position of every token of the full layout, [T, 3].
+
+    The REDtech article (section 3.2) updates the mRoPE positions of the
+    compressed sequence without stating a rule; the reading taken is that a
+    kept token keeps its position in the full request under the Qwen-VL
+    multimodal scheme: walking a request in token order with an index i from
+    0, a text token takes (i, i, i) and moves i on by 1; an image of rows x
+    cols takes, for its token (row, col), (i, i + row, i + col), and moves i
+    on by max(rows, cols)."""
+    pos = np.full((prob.T, 3), -1, np.int64)
+    for b in range(prob.B):
+        lo, hi = int(prob.cu_seqlens[b]), int(prob.cu_seqlens[b + 1])
+        starts = {int(prob.img_start[s]): s for s in range(prob.cu_images[b], prob.cu_images[b + 1])}
+        t, i = lo, 0
+        while t < hi:
+            if t in starts:
+                s = starts[t]
+                rows, cols = int(prob.img_hw[s, 0]), int(prob.img_hw[s, 1])
+                for r in range(rows):
+                    for c in range(cols):
+                        pos[t + r * cols + c] = (i, i + r, i + c)
+                t += rows * cols
+                i += max(rows, cols)
+            else:
+                pos[t] = (i, i, i)
+                t += 1
+                i += 1
+    return pos
 
 
 def compact_loop(prob, keep):

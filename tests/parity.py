@@ -16,9 +16,10 @@ Tolerances (written here, used by every GPU test):
   4 tau then the candidates with m_(k+1) - 2 tau <= m <= m_(k) + 2 tau may be
   chosen freely (the count must still be k); everything above the band must
   be kept and everything below it dropped.
-* compaction and gather: bit-exact against the oracle's compaction of the
-  oracle's flags whenever the kept sets agree; otherwise checked for validity
-  against the GPU's own flags (order, bounds, spatial indices, counts, rows).
+* compaction, gather and rotary positions: bit-exact against the oracle's
+  compaction of the oracle's flags whenever the kept sets agree; otherwise
+  checked for validity against the GPU's own flags (order, bounds, spatial
+  indices, counts, rows, each token's full-layout position).
 """
 from __future__ import annotations
 
@@ -143,6 +144,9 @@ def check_compaction_valid(prob, keep, comp, emb=None):
     if emb is not None:
         assert torch.equal(comp["emb"].view(torch.uint8) if comp["emb"].dtype != torch.uint8 else comp["emb"],
                            emb[torch.from_numpy(tok)].view(torch.uint8))
+    if "positions" in comp:
+        # Each kept token keeps its full-layout rotary position.
+        assert np.array_equal(comp["positions"].numpy(), oracle.rope_positions(prob)[tok])
 
 
 def check_compaction_exact(prob, comp, ref_comp, emb=None):
@@ -153,6 +157,8 @@ def check_compaction_exact(prob, comp, ref_comp, emb=None):
     if emb is not None:
         want = emb[torch.from_numpy(ref_comp["token_idx"])]
         assert torch.equal(comp["emb"].view(torch.uint8), want.view(torch.uint8))
+    if "positions" in comp:
+        assert np.array_equal(comp["positions"].numpy(), ref_comp["positions"])
 
 
 def full_check(prob, got, ref, emb=None):

@@ -164,6 +164,16 @@ def test_workspace_sizes_and_shortfall(lib):
     assert rc == B.TSEL_EWORKSPACE
 
 
+def test_mrope_validation(lib):
+    lay = good_layout()
+    f = lib.tsel_mrope_positions
+    assert f(ctypes.byref(lay.c), FAKE, FAKE, -1, FAKE, FAKE, 64, None) == B.TSEL_EINVAL
+    assert f(ctypes.byref(lay.c), None, FAKE, 4, FAKE, FAKE, 64, None) == B.TSEL_EINVAL
+    need = lib.tsel_workspace_size(B.TSEL_OP_MROPE, None, ctypes.byref(lay.c))
+    assert need == 4 * 2
+    assert f(ctypes.byref(lay.c), FAKE, FAKE, 4, FAKE, FAKE, need - 1, None) == B.TSEL_EWORKSPACE
+
+
 def test_compact_rejects_inconsistent_embedding_args(lib):
     lay = good_layout()
     comp = lib.tsel_workspace_size(B.TSEL_OP_COMPACT, None, ctypes.byref(lay.c))

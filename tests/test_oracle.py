@@ -132,6 +132,52 @@ def test_fp8_decoder_matches_format():
     assert mine[0x38] == 1.0 and mine[0x3C] == 1.5
 
 
+def test_rope_positions_hand_example():
+    """The rotary-position reading worked by hand: request A = 3 text tokens,
+    a 2x3 image, 2 text tokens; request B = a 1x4 image, 1 text token."""
+    prob = handmade([(11, [(3, 2, 3)]), (5, [(0, 1, 4)])], np.zeros((16, 1, 4)), np.zeros((16, 1, 4)),
+                    "causal")
+    want = [(0, 0, 0), (1, 1, 1), (2, 2, 2),
+            (3, 3, 3), (3, 3, 4), (3, 3, 5), (3, 4, 3), (3, 4, 4), (3, 4, 5),
+            (6, 6, 6), (7, 7, 7),
+            (0, 0, 0), (0, 0, 1), (0, 0, 2), (0, 0, 3), (4, 4, 4)]
+    assert np.array_equal(O.rope_positions(prob), np.array(want))
+    keep = np.array([1, 0, 1, 1, 0, 1, 0, 1, 1, 0], np.uint8)
+    comp = O.compact(prob, keep)
+    assert np.array_equal(comp["positions"], np.array(want)[comp["token_idx"]])
+    assert [tuple(x) for x in comp["positions"][3:7]] == [(3, 3, 3), (3, 3, 5), (3, 4, 3), (3, 4, 5)]
+
+
+def test_rope_positions_structure_random_layouts():
+    """Every image: one t for all its tokens, h - t = row, w - t = col; the
+    next token after an image sits max(rows, cols) past the image's t; text
+    tokens step by one."""
+    for seed in range(4):
+        p = random_small(300 + seed, "causal", dtype="f32", n_req=3)
+        pos = O.rope_positions(p)
+        assert np.all(pos >= 0)
+        img_of = np.full(p.T, -1)
+        for s in range(p.S):
+            rows, cols = p.img_hw[s]
+            t0 = p.img_start[s]
+            blk = pos[t0:t0 + rows * cols]
+            assert np.all(blk[:, 0] == blk[0, 0])
+            r, c = np.divmod(np.arange(rows * cols), cols)
+            assert np.array_equal(blk[:, 1] - blk[:, 0], r) and np.array_equal(blk[:, 2] - blk[:, 0], c)
+            img_of[t0:t0 + rows * cols] = s
+            nxt = t0 + rows * cols
+            b = np.searchsorted(p.cu_seqlens, t0, side="right") - 1
+            if nxt < p.cu_seqlens[b + 1]:
+                assert pos[nxt, 0] == blk[0, 0] + max(rows, cols)
+        for b in range(p.B):
+            lo = p.cu_seqlens[b]
+            if lo < p.cu_seqlens[b + 1]:
+                assert pos[lo, 0] == 0
+            for t in range(lo + 1, p.cu_seqlens[b + 1]):
+                if img_of[t] < 0 and img_of[t - 1] < 0:
+                    assert tuple(pos[t]) == (pos[t - 1, 0] + 1,) * 3
+
+
 @pytest.mark.parametrize("mask", ["full", "causal"])
 def test_fp8_problem_against_bruteforce(mask):
     """An fp8 problem from the generator (per-tensor factors folded into its
