@@ -193,6 +193,58 @@ def attention_stats(prob, lse_in: Optional[np.ndarray] = None, scale: Optional[f
     return lse, mass
 
 
+def attention_forward(prob, v=None, scale: Optional[float] = None, workers: int = 1,
+                      heads: Optional[Sequence[int]] = None):
+    """The attention layer's forward pass whose softmax normaliser the
+    selection reuses (REDtech article, section 3.2): ``O = softmax(S) V`` per
+    head and row, S the scaled, masked logits over the row's visible keys,
+    plus the LSE.  Returns ``(o [T, Hq, d], lse [Hq, T])`` in float64; rows
+    or heads outside ``heads`` are NaN."""
+    q64, k64 = to_f64(prob.q), to_f64(prob.k)
+    v64 = to_f64(prob.v if v is None else v)
+    hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
+    dv = v64.shape[2]
+    rep = hq // hkv
+    scale = problem_scale(prob, d) if scale is None else scale
+    causal = prob.mask == "causal"
+    segs = attention_segments(prob)
+    heads = list(range(hq)) if heads is None else list(heads)
+    tasks = [(si, h) for h in heads for si in range(len(segs))]
+
+    def run_one(task):
+        si, h = task
+        lo, hi = segs[si][0], segs[si][1]
+        g = h // rep
+        n = hi - lo
+        o = np.empty((n, dv))
+        lse = np.empty(n)
+        for r0 in range(0, n, ROW_BLOCK):
+            r1 = min(n, r0 + ROW_BLOCK)
+            kend = r1 if causal else n
+            S = scale * (q64[lo + r0:lo + r1, h, :] @ k64[lo:lo + kend, g, :].T)
+            if causal:
+                S = np.where(np.arange(kend)[None, :] <= np.arange(r0, r1)[:, None], S, -np.inf)
+            m = S.max(axis=1)
+            lse[r0:r1] = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+            P = np.exp(S - lse[r0:r1, None])
+            o[r0:r1] = P @ v64[lo:lo + kend, g, :]
+        return o, lse
+
+    if workers > 1:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(run_one, tasks))
+    else:
+        results = [run_one(t) for t in tasks]
+    o_all = np.full((prob.T, hq, dv), np.nan)
+    lse_all = np.full((hq, prob.T), np.nan)
+    for (si, h), (o, lse) in zip(tasks, results):
+        lo, hi = segs[si][0], segs[si][1]
+        o_all[lo:hi, h, :] = o
+        lse_all[h, lo:hi] = lse
+    return o_all, lse_all
+
+
 def lse_rows(prob, tokens: Sequence[int], scale: Optional[float] = None) -> np.ndarray:
     """LSE of selected rows, every query head: ``[Hq, len(tokens)]`` float64.
     Each row is the log-sum-exp of its visible logits, one row at a time."""

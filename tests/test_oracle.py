@@ -197,6 +197,43 @@ def test_fp8_problem_against_bruteforce(mask):
         assert abs(mass[c] - float(ref_mass[c])) <= 1e-12 * max(1.0, float(ref_mass[c]))
 
 
+@pytest.mark.parametrize("mask", ["full", "causal"])
+def test_attention_forward_matches_torch_sdpa(mask):
+    """One request: the forward pass equals torch's scaled_dot_product_attention
+    in float64 (GQA heads expanded), and its LSE equals attention_stats'."""
+    p = make_problem("fwd", [(90, [(10, 6, 9)])], 4, 2, 32, "f32", mask, 1.0, 41, ratios=0.5)
+    o, lse = oracle.attention_forward(p)
+    q = torch.from_numpy(O.to_f64(p.q)).permute(1, 0, 2)
+    k = torch.from_numpy(O.to_f64(p.k)).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    v = torch.from_numpy(O.to_f64(p.v)).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=(mask == "causal"))
+    np.testing.assert_allclose(o, want.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-13)
+    lse2, _ = oracle.attention_stats(p)
+    np.testing.assert_allclose(lse, lse2, rtol=1e-14)
+
+
+def test_attention_forward_invariants():
+    """Rows of P sum to one (V = 1 gives O = 1), and with V the identity on
+    the keys O is P itself, whose candidate columns summed over rows and heads
+    give attention_stats' mass (two separate code paths)."""
+    p = random_small(42, "causal", dtype="f32", hq=2, hkv=1, d=64, n_req=1)
+    T = p.T
+    ones = torch.ones((T, 1, 64), dtype=torch.float32)
+    o, _ = oracle.attention_forward(p, v=ones)
+    np.testing.assert_allclose(o, 1.0, rtol=1e-13)
+    eye = torch.zeros((T, 1, T), dtype=torch.float32)
+    eye[torch.arange(T), 0, torch.arange(T)] = 1.0
+    pq = make_problem("fwd_eye", [(T, [(int(p.img_start[s]), int(p.img_hw[s, 0]), int(p.img_hw[s, 1]))
+                                       for s in range(p.S)])], 2, 1, 64, "f32", "causal", 1.0, 42,
+                      ratios=0.5)
+    pq.q, pq.k = p.q, p.k
+    o, _ = oracle.attention_forward(pq, v=eye, scale=1 / math.sqrt(64))
+    _, mass = oracle.attention_stats(pq)
+    cand_tok = np.concatenate([np.arange(pq.img_start[s], pq.img_start[s] + pq.img_hw[s, 0] * pq.img_hw[s, 1])
+                               for s in range(pq.S)])
+    np.testing.assert_allclose(o.sum(axis=(0, 1))[cand_tok], mass, rtol=1e-12)
+
+
 def test_two_keys_logistic_closed_form():
     """Full mask, two tokens: P(i -> key 0) = sigmoid(s_i0 - s_i1)."""
     rng = np.random.default_rng(3)

@@ -16,7 +16,10 @@ Recipe (numpy ``default_rng(seed)``, PCG64), in draw order:
 
 Embedding rows (standard normals) come from their own stream,
 ``default_rng([seed, 1])``, drawn on first use: a gather copies bytes, so
-the rows are only needed by the compaction checks and the benchmark.
+the rows are only needed by the compaction checks and the benchmark.  The
+values V of the layer's attention (standard normals, [T, Hkv, d], in the
+Q/K storage type; bf16 for fp8 problems), used only by the attention
+forward, come from ``default_rng([seed, 2])``, also drawn on first use.
 
 Q/K/emb are generated in fp32 and then rounded to the storage dtype with
 round-to-nearest-even (torch ``.to``), so every consumer reads the same
@@ -79,6 +82,20 @@ class Problem:
     dominant: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
     softmax_scale: Optional[float] = None   # None: 1/sqrt(d)
     _emb: Optional[torch.Tensor] = None
+    _v: Optional[torch.Tensor] = None
+
+    @property
+    def v(self) -> torch.Tensor:
+        """Attention values [T, Hkv, d] (drawn on first use)."""
+        if self._v is None:
+            rng = np.random.default_rng([self.seed, 2])
+            x = rng.standard_normal((self.T, self.hkv, self.d), dtype=np.float32)
+            self._v = _round(x, "bf16" if self.dtype == "fp8" else self.dtype)
+        return self._v
+
+    @v.setter
+    def v(self, value: torch.Tensor):
+        self._v = value
 
     @property
     def emb(self) -> torch.Tensor:
