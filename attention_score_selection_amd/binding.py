@@ -21,6 +21,7 @@ TSEL_F32, TSEL_F16, TSEL_BF16, TSEL_FP8_E4M3 = 0, 1, 2, 3
 MASKS = {"full": 0, "causal": 1, "blockdiag": 2}
 TSEL_OP_LSE, TSEL_OP_COLSCORE, TSEL_OP_TOPK, TSEL_OP_COMPACT, TSEL_OP_MROPE = 0, 1, 2, 3, 4
 EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact", "tsel_mrope_positions",
+           "tsel_attention_fwd",
            "tsel_workspace_size", "tsel_last_error", "tsel_version")
 
 _DTYPES = {torch.float32: TSEL_F32, torch.float16: TSEL_F16, torch.bfloat16: TSEL_BF16,
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.tsel_compact.argtypes = [ctypes.POINTER(CLayout), _P, _P, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]
+        L.tsel_attention_fwd.restype = ctypes.c_int
+        L.tsel_attention_fwd.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P,
+                                         ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_int64,
+                                         ctypes.c_int64, _P, _P]
         L.tsel_mrope_positions.restype = ctypes.c_int
         L.tsel_mrope_positions.argtypes = [ctypes.POINTER(CLayout), _P, _P, ctypes.c_int32, _P, _P,
                                            ctypes.c_size_t, _P]
@@ -233,6 +238,23 @@ def tsel_compact(layout: Layout, keep: torch.Tensor, k_per_pool, emb: Optional[t
                               _ptr(o["cu_seqlens"]), _ptr(o["img_counts"]), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(dev)))
     return o
+
+
+def tsel_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, layout: Layout, mask: str,
+                       softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None):
+    """Attention forward: out [T, Hq, d] in q's dtype and the LSE fp32 [Hq, T]."""
+    attn = make_attn(q, k, mask, softmax_scale)
+    if v.dim() != 3 or v.dtype != q.dtype or v.stride(2) != 1 or v.shape != k.shape:
+        raise ValueError("v must be [T, Hkv, d] like k, with a contiguous last dimension")
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((q.shape[1], layout.T), dtype=torch.float32, device=q.device)
+    _check(lib().tsel_attention_fwd(ctypes.byref(attn), ctypes.byref(layout.c), _ptr(v), v.stride(0),
+                                    v.stride(1), _ptr(out), out.stride(0), out.stride(1), _ptr(lse),
+                                    _stream(q.device)))
+    return out, lse
 
 
 def tsel_mrope_positions(layout: Layout, compact: dict, out: Optional[torch.Tensor] = None,

@@ -152,6 +152,26 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   return TSEL_OK;
 }
 
+// Attention forward: row blocks of 4 waves x one resident 32-row group.
+int plan_fwd(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
+  plan_common(a, l, p);
+  if (int rc = check_offsets(a, l, p->F)) return rc;
+  p->NT = 1;
+  p->TB = 4 * 32 / p->F;
+  long long R = 0;
+  for (int s = 0; s < p->nseg; ++s) {
+    long long n, nc;
+    seg_sizes(l, p->segkind, s, n, nc);
+    R += (n + p->TB - 1) / p->TB;
+  }
+  p->jobs_per_hb = R;
+  p->total_jobs = R * p->nhb;
+  p->KB = p->RC = p->RCmax = 0;
+  p->partial_bytes = 0;
+  if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
+  return TSEL_OK;
+}
+
 // Key blocks of 4 waves x NG resident 32-key groups; row chunks of ~8192
 // streamed rows, halved while the grid is small.  One partial per
 // (head block, row chunk, candidate).
@@ -384,6 +404,46 @@ int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *e
     e = launch_gather(emb, emb_stride, emb_row_bytes, out_emb, out_emb_stride, out_token_idx, c.total,
                       out_capacity, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_compact launch: %s", hipGetErrorString(e));
+  return TSEL_OK;
+}
+
+int tsel_attention_fwd(const tsel_attn_t *attn, const tsel_layout_t *layout, const void *v,
+                       int64_t v_stride_tok, int64_t v_stride_head, void *out, int64_t out_stride_tok,
+                       int64_t out_stride_head, float *lse, void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc == TSEL_OK) rc = check_attn(attn, layout);
+  if (rc != TSEL_OK) return rc;
+  if (attn->dtype != TSEL_BF16 && attn->dtype != TSEL_F16)
+    return fail(TSEL_EUNSUPPORTED, "the attention forward takes bf16 or f16 inputs");
+  const long long es = elem_size(attn->dtype);
+  if (layout->total_tokens > 0) {
+    if (v == nullptr || out == nullptr || lse == nullptr)
+      return fail(TSEL_EINVAL, "v, out and lse are required");
+    if ((uintptr_t)v & 15) return fail(TSEL_EINVAL, "v must be 16-byte aligned");
+    if ((uintptr_t)out & 7) return fail(TSEL_EINVAL, "out must be 8-byte aligned");
+    if ((uintptr_t)lse & 3) return fail(TSEL_EINVAL, "lse must be 4-byte aligned");
+  }
+  if (v_stride_tok <= 0 || v_stride_head <= 0 || (v_stride_tok * es) % 16 || (v_stride_head * es) % 16)
+    return fail(TSEL_EINVAL, "v strides must be positive and multiples of 16 bytes");
+  if (out_stride_tok <= 0 || out_stride_head <= 0 || (out_stride_tok * es) % 8 ||
+      (out_stride_head * es) % 8)
+    return fail(TSEL_EINVAL, "out strides must be positive and multiples of 8 bytes");
+  if (32LL * v_stride_tok * es >= kBufferLimit)
+    return fail(TSEL_EUNSUPPORTED, "strides too large: a 32-row tile spans 2 GiB or more");
+  AttnPlan p;
+  if ((rc = plan_fwd(attn, layout, &p)) != TSEL_OK) return rc;
+  FwdArgs x{};
+  x.at = attn_args(attn, layout, p);
+  x.at.lse_out = lse;
+  x.v = v;
+  x.v_st = v_stride_tok;
+  x.v_sh = v_stride_head;
+  x.out = out;
+  x.o_st = out_stride_tok;
+  x.o_sh = out_stride_head;
+  hipError_t e = launch_fwd(p, x, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_attention_fwd launch: %s", hipGetErrorString(e));
   return TSEL_OK;
 }
 

@@ -46,6 +46,15 @@ struct AttnArgs {
   int N, RC, RCmax, KB;  // candidates, row-chunk tokens, max chunks per segment, keys per block
 };
 
+// Attention forward: the LSE kernel's job split plus the values and output.
+struct FwdArgs {
+  AttnArgs at;           // q, k, layout, head fold, masks, TB, lse_out
+  const void *v;
+  long long v_st, v_sh;  // element strides of v
+  void *out;
+  long long o_st, o_sh;  // element strides of out
+};
+
 // Host-side plan of one attention launch.
 struct AttnPlan {
   int dtype, D, NT;
@@ -65,6 +74,8 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
 // Kernel launchers (attn.hip / select.hip).  Return hipError_t of the launch.
 hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, hipStream_t s);
 hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, float *score, hipStream_t s);
+hipError_t launch_fwd(const AttnPlan &p, const FwdArgs &a, hipStream_t s);
+int plan_fwd(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
 
 struct TopkChunk {
   int b0;        // first pool of this launch

@@ -99,6 +99,29 @@ def cpu_baseline(prob, elems_per_head, budget_s=10.0):
                       f"({done} KV group(s), {elems:.4g} elements) of the same workload, {dt:.1f} s"}
 
 
+def time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems):
+    """The layer's attention forward (O and LSE) timed with HIP events;
+    4*d flops per visible (head, row, key) pair (QK^T and PV)."""
+    import torch
+    if prob.dtype not in ("bf16", "f16"):
+        return {"skipped": "the forward takes bf16/f16 inputs"}
+    v = prob.v.to(dev)
+    out = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    lse = torch.empty((prob.hq, prob.T), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        tsel.tsel_attention_fwd(q, k, v, lay, prob.mask, 0.0, out=out, lse=lse)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        tsel.tsel_attention_fwd(q, k, v, lay, prob.mask, 0.0, out=out, lse=lse)
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    t = ev[0].elapsed_time(ev[1]) / 1e3 / args.steps
+    flops = 4.0 * prob.d * lse_elems
+    return {"ms": t * 1e3, "tflops": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / peak,
+            "flops_per_launch": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +130,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
+    ap.add_argument("--forward", action="store_true",
+                    help="also time the attention forward (tsel_attention_fwd) on the same layer")
     ap.add_argument("--dtype", choices=("bf16", "fp8"), default="bf16",
                     help="Q/K storage type of the workload (fp8: OCP E4M3 with per-tensor factors)")
     args = ap.parse_args()
@@ -211,6 +236,8 @@ def main():
                      "frac": achieved / peak,
                      "traffic": stored_traffic(prob.name, dominant[0])},
     }
+    if args.forward:
+        result["attention_forward"] = time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems)
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

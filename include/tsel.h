@@ -176,6 +176,20 @@ int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *e
                  int32_t *out_cu_seqlens, int32_t *out_img_counts, void *workspace,
                  size_t workspace_bytes, void *stream);
 
+/* Attention forward of the layer whose softmax normaliser the selection
+ * reuses (REDtech article, section 3.2: the FlashAttention pass already
+ * produces the LSE): for every query head h and row i,
+ *   out[i, h, :] = sum_j softmax_j(scale * q_{i,h} . k_{j,g(h)}) v[j, g(h), :]
+ * over the row's visible keys (the masks and segments of tsel_lse), and
+ * lse[h, i] exactly as tsel_lse computes it.  bf16 or f16 inputs only
+ * (TSEL_EUNSUPPORTED otherwise); v is [T, Hkv, head_dim] in the same type,
+ * 16-byte aligned, strides (elements) multiples of 16 bytes; out is
+ * [T, Hq, head_dim] in the same type, 8-byte aligned, strides multiples of
+ * 8 bytes; lse fp32 [Hq, T].  No workspace. */
+int tsel_attention_fwd(const tsel_attn_t *attn, const tsel_layout_t *layout, const void *v,
+                       int64_t v_stride_tok, int64_t v_stride_head, void *out, int64_t out_stride_tok,
+                       int64_t out_stride_head, float *lse, void *stream);
+
 /* Rotary position ids of the compacted sequence, for a prefill that takes it
  * (REDtech article, section 3.2: the mRoPE positions are updated together
  * with lengths, image boundaries and spatial indices so the shorter sequence

@@ -265,6 +265,28 @@ def lse_rows(prob, tokens: Sequence[int], scale: Optional[float] = None) -> np.n
     return out
 
 
+def forward_rows(prob, tokens: Sequence[int], v=None, scale: Optional[float] = None) -> np.ndarray:
+    """Attention-forward output of selected rows, every query head:
+    ``[len(tokens), Hq, dv]`` float64, one row at a time (softmax of the
+    row's visible logits times the values)."""
+    q64, k64 = to_f64(prob.q), to_f64(prob.k)
+    v64 = to_f64(prob.v if v is None else v)
+    hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
+    rep = hq // hkv
+    scale = problem_scale(prob, d) if scale is None else scale
+    segs = attention_segments(prob)
+    out = np.full((len(tokens), hq, v64.shape[2]), np.nan)
+    for row, t in enumerate(tokens):
+        for lo, hi, _b, _loc, _glob in segs:
+            if lo <= t < hi:
+                kend = t + 1 if prob.mask == "causal" else hi
+                for h in range(hq):
+                    z = scale * (k64[lo:kend, h // rep, :] @ q64[t, h, :])
+                    p = np.exp(z - z.max())
+                    out[row, h] = (p / p.sum()) @ v64[lo:kend, h // rep, :]
+    return out
+
+
 def request_of_candidate(prob) -> np.ndarray:
     """Request index of every candidate."""
     out = np.empty(prob.N, np.int64)

@@ -164,6 +164,23 @@ def test_workspace_sizes_and_shortfall(lib):
     assert rc == B.TSEL_EWORKSPACE
 
 
+def test_attention_fwd_validation(lib):
+    lay = good_layout()
+    f = lib.tsel_attention_fwd
+    a = attn(dtype=B.TSEL_F32)
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 256, 128, FAKE, 1024, 128, FAKE, None) == \
+        B.TSEL_EUNSUPPORTED
+    assert "bf16 or f16" in last_error(lib)
+    a = attn()
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), None, 256, 128, FAKE, 1024, 128, FAKE, None) == B.TSEL_EINVAL
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE + 8, 256, 128, FAKE, 1024, 128, FAKE, None) == \
+        B.TSEL_EINVAL
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 256, 128, FAKE + 2, 1024, 128, FAKE, None) == \
+        B.TSEL_EINVAL
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 250, 128, FAKE, 1024, 128, FAKE, None) == B.TSEL_EINVAL
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 256, 128, FAKE, 1023, 128, FAKE, None) == B.TSEL_EINVAL
+
+
 def test_mrope_validation(lib):
     lay = good_layout()
     f = lib.tsel_mrope_positions

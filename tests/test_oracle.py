@@ -212,6 +212,15 @@ def test_attention_forward_matches_torch_sdpa(mask):
     np.testing.assert_allclose(lse, lse2, rtol=1e-14)
 
 
+def test_forward_rows_equal_attention_forward():
+    """The row-at-a-time forward agrees with the blocked one (two code paths)."""
+    for mask in ("full", "causal", "blockdiag"):
+        p = random_small(43, mask, dtype="bf16", hq=4, hkv=2, d=64, n_req=2)
+        o, _ = oracle.attention_forward(p)
+        rows = np.arange(0, p.T, 7)
+        np.testing.assert_allclose(oracle.forward_rows(p, rows), o[rows], rtol=1e-12, atol=1e-14)
+
+
 def test_attention_forward_invariants():
     """Rows of P sum to one (V = 1 gives O = 1), and with V the identity on
     the keys O is P itself, whose candidate columns summed over rows and heads
