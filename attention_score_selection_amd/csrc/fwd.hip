@@ -14,7 +14,8 @@
 // registers (converted to the input type) and V^T comes from an LDS copy of
 // the value tile stored transposed.  The contraction's k slots of lane half h
 // are the keys 16c + {0..3, 8..11} + 4h of chunk c, which is how the S^T
-// accumulator already holds them; the V^T fragment is read in that order.
+// accumulator already holds them; the transposed copy stores the keys in that
+// order, so a V^T fragment is one 16-byte LDS read.
 //
 // The running maximum only moves when a tile's maximum exceeds it by more
 // than 2^8 (so P stays below 2^8, safe for f16 operands); the accumulators are
@@ -29,6 +30,12 @@ constexpr float kRescale = 8.0f;  // log2 headroom before the running max moves
 
 // Transposed LDS copy of one 32-key value tile: row d (one per value column,
 // padded to whole 32-row groups) holds the 32 keys' values, VS bytes apart.
+// Within each 16-key chunk the keys are stored in the order 0-3, 8-11, 4-7,
+// 12-15, so the eight keys one lane half contracts over (16c + {0..3, 8..11}
+// + 4h) are adjacent: one 16-byte read per fragment.
+__device__ __forceinline__ constexpr int vt_slot(int key) {
+  return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
 template <int DT, int D>
 struct VGeom {
   static constexpr int ES = Elem<DT>::ES;
@@ -70,7 +77,7 @@ struct VStage {
     const int db = threadIdx.x >> 4;
     const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
     const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
-    char *col = vt + (8 * db) * VG::VS + key0 * VG::ES;
+    char *col = vt + (8 * db) * VG::VS + vt_slot(key0) * VG::ES;  // key0 + 1 is the next slot
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // Column 8db + 2i: low halves of a[i] and b[i]; column 8db + 2i + 1:
@@ -101,16 +108,15 @@ __device__ __forceinline__ Chunk<DT> pack_p(const float (&p)[16], int c) {
 }
 
 // V^T fragment of row group dg, key chunk c: lane row dg*32 + lane%32, keys
-// 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (h = lane / 32).
+// 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (h = lane / 32), stored
+// adjacently at slots 16c + 8h .. +7.
 template <int DT, int D>
 __device__ __forceinline__ Chunk<DT> read_vt(const char *vt, int dg, int c) {
   using VG = VGeom<DT, D>;
   const int lane = lane_id();
-  const char *row = vt + (dg * 32 + (lane & 31)) * VG::VS + (16 * c + 4 * (lane >> 5)) * VG::ES;
-  const uint2 lo = *reinterpret_cast<const uint2 *>(row);
-  const uint2 hi = *reinterpret_cast<const uint2 *>(row + 8 * VG::ES);
+  const char *row = vt + (dg * 32 + (lane & 31)) * VG::VS + (16 * c + 8 * (lane >> 5)) * VG::ES;
   Chunk<DT> r;
-  r.v[0] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  r.v[0] = *reinterpret_cast<const uint4 *>(row);
   return r;
 }
 
