@@ -27,7 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6,   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
-               "fp8": 5033.2}    # dense fp8 MFMA: twice the bf16 rate
+               "f16": 2516.6,    # same rate for fp16
+               "fp8": 5033.2,    # dense fp8 MFMA: twice the bf16 rate
+               "f32": 157.3}     # fp32 matrix rate
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
 
@@ -132,6 +134,9 @@ def main():
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
     ap.add_argument("--forward", action="store_true",
                     help="also time the attention forward (tsel_attention_fwd) on the same layer")
+    ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=4,
+                    help="named workload (default 4: the 16384-token GQA decoder layer); the others are "
+                         "parity workloads, timed here for reference only")
     ap.add_argument("--dtype", choices=("bf16", "fp8"), default="bf16",
                     help="Q/K storage type of the workload (fp8: OCP E4M3 with per-tensor factors)")
     args = ap.parse_args()
@@ -148,9 +153,12 @@ def main():
     import attention_score_selection_amd as tsel
     from workloads import make_config
 
-    prob = make_config(4) if args.dtype == "bf16" else make_config(4, dtype=args.dtype)
+    if args.dtype == "bf16":
+        prob = make_config(args.config)
+    else:
+        prob = make_config(args.config, dtype=args.dtype)
     scale = prob.softmax_scale if prob.softmax_scale is not None else 0.0
-    peak = PEAK_TFLOPS[args.dtype]
+    peak = PEAK_TFLOPS[prob.dtype]
     dev = torch.device("cuda:0")
     lay = tsel.Layout.from_problem(prob, dev)
     q, k, emb = prob.q.to(dev), prob.k.to(dev), prob.emb.to(dev)
@@ -175,9 +183,14 @@ def main():
     ws_rope = torch.empty((max(4, tsel.tsel_workspace_size(4, lay)),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    # A workload with a supplied LSE (the reuse path) takes it as an input: it
+    # is computed once here, outside the timed step.
+    tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse)
+
     def step(ev=None):
         if ev: ev[0].record(stream)
-        tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse)
+        if not prob.lse_supplied:
+            tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse)
         if ev: ev[1].record(stream)
         tsel.tsel_colscore(q, k, lay, prob.mask, lse, scale, out=score, workspace=ws_col)
         if ev: ev[2].record(stream)
@@ -203,7 +216,8 @@ def main():
 
     col_flops = 2.0 * d * col_elems
     lse_flops = 2.0 * d * lse_elems
-    dominant = ("tsel_colscore", t_col, col_flops) if t_col >= t_lse else ("tsel_lse", t_lse, lse_flops)
+    dominant = (("tsel_colscore", t_col, col_flops) if (t_col >= t_lse or prob.lse_supplied)
+                else ("tsel_lse", t_lse, lse_flops))
     achieved = dominant[2] / dominant[1] / 1e12
     kept = int(np.sum(ks))
     row_bytes = prob.emb_dim * emb.element_size()
@@ -215,20 +229,22 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": args.dtype,
-        "data": "synthetic (seeded normal Q/K, std 1/sqrt(d)" +
-                (", quantised to fp8 E4M3 with per-tensor factors" if args.dtype == "fp8" else "") +
-                "; normal bf16 embeddings)",
+        "dtype": prob.dtype,
+        "data": f"synthetic (seeded normal Q/K, std {prob.std:.4g}" +
+                (", quantised to fp8 E4M3 with per-tensor factors" if prob.dtype == "fp8" else "") +
+                f"; normal {prob.emb_dtype} embeddings)",
         "config": {"workload": prob.name, "tokens": prob.T, "heads_q": prob.hq, "heads_kv": prob.hkv,
                    "head_dim": d, "mask": prob.mask, "vision_candidates": prob.N, "images": prob.S,
-                   "keep_ratio": float(ratios[0]), "kept_vision": kept, "tokens_out": t_out,
-                   "emb_dim": prob.emb_dim, "lse": "computed in-library"},
+                   "keep_ratio": float(ratios[0]) if len(ratios) == 1 else [float(r) for r in ratios],
+                   "kept_vision": kept, "tokens_out": t_out,
+                   "emb_dim": prob.emb_dim,
+                   "lse": "supplied (not timed)" if prob.lse_supplied else "computed in-library"},
         "phases_ms": {"lse": t_lse * 1e3, "colscore": t_col * 1e3, "budget_topk": t_topk * 1e3,
                       "compact_gather": t_cmp * 1e3, "rope_positions": t_rope * 1e3},
         "colscore_elements_per_s": col_elems / t_col,
         "colscore_mfma_frac": col_flops / t_col / 1e12 / peak,
-        "lse_elements_per_s": lse_elems / t_lse,
-        "lse_mfma_frac": lse_flops / t_lse / 1e12 / peak,
+        "lse_elements_per_s": None if prob.lse_supplied else lse_elems / t_lse,
+        "lse_mfma_frac": None if prob.lse_supplied else lse_flops / t_lse / 1e12 / peak,
         "kept_tokens_per_s": kept / (t_topk + t_cmp),
         "select_gather_GBps": gather_bytes / (t_topk + t_cmp) / 1e9,
         "roofline": {"kernel": dominant[0], "bound": "mfma", "achieved": achieved,
