@@ -53,6 +53,76 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total) {
   return res;
 }
 
+// Pools of up to kTopkThreads * kTopkRegKeys candidates: every thread holds
+// a contiguous run of at most kTopkRegKeys keys in registers for all passes.
+// Histogram adds are merged per thread while consecutive keys share a digit
+// (the keys of one pool often share their leading digits), and the final
+// ordered admission of keys equal to tau needs one block scan of per-thread
+// counts.
+constexpr int kTopkRegKeys = 32;
+
+__device__ __forceinline__ void topk_registers(const float *score, int n, int k, uint8_t *keep,
+                                               int *hist, int *sh, int &s_digit, int &s_above) {
+  const int tid = threadIdx.x;
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  uint32_t u[kTopkRegKeys];
+#pragma unroll
+  for (int j = 0; j < kTopkRegKeys; ++j) u[j] = (i0 + j < i1) ? score_key(score[i0 + j]) : 0u;
+  uint32_t prefix = 0u, pmask = 0u;
+  int kr = k;  // how many of the keys matching `prefix` must still be kept
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    int cur = -1, cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkRegKeys; ++j) {
+      if (i0 + j < i1 && (u[j] & pmask) == prefix) {
+        const int d = (int)((u[j] >> shift) & 255u);
+        if (d != cur) {
+          if (cnt) atomicAdd(&hist[cur], cnt);
+          cur = d;
+          cnt = 0;
+        }
+        ++cnt;
+      }
+    }
+    if (cnt) atomicAdd(&hist[cur], cnt);
+    __syncthreads();
+    // Suffix counts over digits: scan the histogram from digit 255 down.
+    const int hv = (tid < 256) ? hist[255 - tid] : 0;
+    int tot;
+    const int excl = block_excl_scan(hv, sh, tot);
+    if (tid < 256) {
+      const int above = excl, upto = excl + hv;
+      if (above < kr && upto >= kr) {
+        s_digit = 255 - tid;
+        s_above = above;
+      }
+    }
+    __syncthreads();
+    kr -= s_above;
+    prefix |= (uint32_t)s_digit << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  // prefix = tau; the kr lowest-index keys equal to tau are kept.
+  int eq = 0;
+#pragma unroll
+  for (int j = 0; j < kTopkRegKeys; ++j) eq += (i0 + j < i1 && u[j] == prefix) ? 1 : 0;
+  int tot;
+  int rank = block_excl_scan(eq, sh, tot);
+#pragma unroll
+  for (int j = 0; j < kTopkRegKeys; ++j) {
+    if (i0 + j < i1) {
+      const bool e = u[j] == prefix;
+      keep[i0 + j] = (u[j] > prefix || (e && rank < kr)) ? 1 : 0;
+      rank += e ? 1 : 0;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const float *score,
                                                            TopkChunk ks, uint8_t *keep) {
   __shared__ int hist[256];
@@ -68,6 +138,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const f
   if (k <= 0 || k >= n) {
     const uint8_t f = (k >= n) ? 1 : 0;
     for (int i = tid; i < n; i += kTopkThreads) keep[lo + i] = f;
+    return;
+  }
+  if (n <= kTopkThreads * kTopkRegKeys) {
+    topk_registers(score + lo, n, k, keep + lo, hist, sh, s_digit, s_above);
     return;
   }
   uint32_t prefix = 0u, pmask = 0u;
