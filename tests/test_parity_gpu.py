@@ -318,3 +318,35 @@ def test_deterministic_repeat(dev):
     assert np.array_equal(a["keep"], b["keep"])
     for key in a["compact"]:
         assert torch.equal(a["compact"][key], b["compact"][key])
+
+
+@pytest.mark.parametrize("pattern", ["distinct", "ties", "nonfinite"])
+def test_budget_topk_synthetic_scores_all_pool_sizes(dev, pattern):
+    """tsel_budget_topk alone on synthetic fp32 scores (drawn here, not by the
+    GPU path), pools on both sides of the register-resident limit (32768)
+    and past it, against the oracle's rank rule exactly."""
+    sizes = [5, 1000, 1023, 32768, 32769, 50000]
+    reqs, off = [], 0
+    for n in sizes:
+        side = int(np.ceil(np.sqrt(n)))
+        while n % side:
+            side -= 1
+        reqs.append((n + 3, [(2, n // side, side)]))
+    prob = make_problem("topk_pools_" + pattern, reqs, 1, 1, 64, "bf16", "causal", 1.0, 37,
+                        ratio_range=(0.1, 0.9), emb_dim=4)
+    rng = np.random.default_rng(38)
+    score = (rng.random(prob.N) * 1e-4 + 3e-5).astype(np.float32)
+    if pattern == "ties":
+        score = np.round(score * 2e5).astype(np.float32) / np.float32(2e5)  # ~20 distinct values
+    if pattern == "nonfinite":
+        idx = rng.choice(prob.N, size=prob.N // 50, replace=False)
+        score[idx[0::3]] = np.nan
+        score[idx[1::3]] = np.inf
+        score[idx[2::3]] = -np.inf
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    keep, ks = tsel.tsel_budget_topk(lay, torch.from_numpy(score).to(dev), prob.keep_ratio)
+    torch.cuda.synchronize(dev)
+    ref_keep, ref_k = oracle.topk(prob, score.astype(np.float64))
+    assert np.array_equal(ks, ref_k)
+    assert np.array_equal(keep.cpu().numpy(), ref_keep)
