@@ -12,6 +12,12 @@
  *   tsel_budget_topk  one top-k per request pool, k = floor(r * N + 1e-6)
  *   tsel_compact      stable compaction and gather of the kept tokens
  *
+ * and two calls sit on either side of it:
+ *
+ *   tsel_attention_fwd    the layer's attention forward, which yields the LSE
+ *                         the selection can reuse instead of tsel_lse
+ *   tsel_mrope_positions  rotary positions of the compacted sequence
+ *
  * Sources: LiteVLM (arXiv 2506.07416) review, section 3.2 (token selection
  * module) and its formula section (score of a vision token = the attention it
  * receives; softmax(QK^T / sqrt(d))); REDtech "vision token compression + SERE"
@@ -47,7 +53,7 @@
 extern "C" {
 #endif
 
-#define TSEL_VERSION 1
+#define TSEL_VERSION 2
 
 #define TSEL_OK 0
 #define TSEL_EINVAL (-1)      /* bad pointer, size, offset, ratio or layout        */

@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_path(lib):
     names = declared_functions()
-    for n in ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact"):
+    for n in ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact", "tsel_attention_fwd",
+              "tsel_mrope_positions"):
         assert n in names
     assert set(names) == set(B.EXPORTS)
 
@@ -45,7 +46,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version(lib):
-    assert lib.tsel_version() == 1
+    header = open(HEADER).read()
+    want = int(re.search(r"#define TSEL_VERSION (\d+)", header).group(1))
+    assert lib.tsel_version() == want == 2
 
 
 FAKE = 4096  # non-null device address that validation never dereferences
