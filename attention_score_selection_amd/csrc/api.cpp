@@ -2,6 +2,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <algorithm>
 #include <string>
@@ -225,6 +226,86 @@ static DevLayout dev_layout(const tsel_layout_t *l) {
   return L;
 }
 
+// Work of each job of one head block, in 32-row tiles streamed, in the
+// kernels' enumeration (segment by segment).  Row-block jobs (LSE, forward):
+// a causal segment's row blocks are enumerated last first and see keys up to
+// their last token; otherwise every row block sees the whole segment.
+// Key-block jobs (column score, row chunk rc x key block kb): the rows of the
+// chunk from the first one that sees the block's first key.  One tile more
+// per job stands for its setup.
+static void job_weights(const tsel_attn_t *a, const tsel_layout_t *l, const AttnPlan &p, bool keyblocks,
+                        std::vector<int> &w) {
+  const bool causal = a->mask == TSEL_MASK_CAUSAL;
+  w.clear();
+  for (int s = 0; s < p.nseg; ++s) {
+    long long lo, hi, sl, sh;
+    if (p.segkind == SEG_REQ) {
+      lo = l->cu_seqlens_h[s];
+      hi = l->cu_seqlens_h[s + 1];
+      sl = l->cu_images_h[s];
+      sh = l->cu_images_h[s + 1];
+    } else {
+      lo = l->img_start_h[s];
+      hi = lo + (long long)l->img_hw_h[2 * s] * l->img_hw_h[2 * s + 1];
+      sl = s;
+      sh = s + 1;
+    }
+    if (!keyblocks) {
+      const long long nrb = (hi - lo + p.TB - 1) / p.TB;
+      for (long long loc = 0; loc < nrb; ++loc) {
+        const long long rb = causal ? nrb - 1 - loc : loc;
+        const long long keys = causal ? std::min((rb + 1) * p.TB, hi - lo) : hi - lo;
+        w.push_back((int)((keys + 31) / 32 + 1));
+      }
+      continue;
+    }
+    const long long cl = l->cu_cands_h[sl], ch = l->cu_cands_h[sh];
+    const long long nkb = (ch - cl + p.KB - 1) / p.KB, nrc = (hi - lo + p.RC - 1) / p.RC;
+    const long long tpt = 32 / p.F;
+    for (long long rc = 0; rc < nrc; ++rc)
+      for (long long kb = 0; kb < nkb; ++kb) {
+        const long long c_lo = lo + rc * p.RC, c_hi = std::min(c_lo + p.RC, hi);
+        long long r_lo = c_lo;
+        if (causal) {
+          const long long c = cl + kb * p.KB;
+          long long img = sl;
+          while (img + 1 < sh && l->cu_cands_h[img + 1] <= c) ++img;
+          r_lo = std::max(c_lo, (long long)l->img_start_h[img] + (c - l->cu_cands_h[img]));
+        }
+        w.push_back((int)(std::max(0LL, (c_hi - r_lo + tpt - 1) / tpt) + 1));
+      }
+  }
+}
+
+// Heaviest-first job order for launches over several segments (varlen
+// batches): jobs are enumerated segment by segment, so without it the light
+// jobs of one request run before the heavy jobs of the next and the tail of
+// the launch grows.  Left in enumeration order when the weights already do
+// not increase (one causal segment, equal segments) or there are too many
+// jobs per head block for the permutation to travel in the arguments.  The
+// column score runs an XCD's jobs rank by rank across its head blocks, the LSE
+// head block by head block.  The forward keeps enumeration order: its jobs
+// also stream V, and mixing requests within an XCD costs it more L2 reuse than
+// the order wins (measured on an 8-request varlen batch).
+static void set_order(AttnArgs &x, const tsel_attn_t *a, const tsel_layout_t *l, const AttnPlan &p,
+                      bool keyblocks, int mode) {
+  x.order = kOrderPlain;
+  memset(x.perm, 0, sizeof(x.perm));
+  if (mode == kOrderPlain || p.nseg < 2 || p.jobs_per_hb > kOrderMaxJobs) return;
+  std::vector<int> w;
+  job_weights(a, l, p, keyblocks, w);
+  if ((long long)w.size() != p.jobs_per_hb) return;
+  bool sorted = true;
+  for (size_t i = 1; i < w.size() && sorted; ++i) sorted = w[i] <= w[i - 1];
+  if (sorted) return;
+  std::vector<int> idx(w.size());
+  for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int)i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int i, int j) { return w[i] > w[j]; });
+  for (size_t i = 0; i < idx.size(); ++i)
+    x.perm[i >> 1] |= (unsigned)idx[i] << (16 * (i & 1));
+  x.order = (mode == kOrderRankMajor && p.nhb % 8 == 0) ? kOrderRankMajor : kOrderSorted;
+}
+
 static AttnArgs attn_args(const tsel_attn_t *a, const tsel_layout_t *l, const AttnPlan &p) {
   AttnArgs x{};
   x.L = dev_layout(l);
@@ -245,6 +326,7 @@ static AttnArgs attn_args(const tsel_attn_t *a, const tsel_layout_t *l, const At
   x.c1 = (float)(scale * 1.4426950408889634074);
   x.jobs_per_hb = (int)p.jobs_per_hb;
   x.total_jobs = (int)p.total_jobs;
+  x.order = kOrderPlain;
   x.TB = p.TB;
   x.N = l->cu_cands_h[l->num_images];
   x.RC = p.RC;
@@ -303,6 +385,7 @@ int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, v
   AttnPlan p;
   if ((rc = plan_lse(attn, layout, &p)) != TSEL_OK) return rc;
   AttnArgs a = attn_args(attn, layout, p);
+  set_order(a, attn, layout, p, false, kOrderSorted);
   a.lse_out = lse;
   const hipError_t e = launch_lse(p, a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_lse launch: %s", hipGetErrorString(e));
@@ -326,6 +409,7 @@ int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const fl
                 workspace_bytes);
   if ((uintptr_t)workspace & 15) return fail(TSEL_EINVAL, "workspace must be 16-byte aligned");
   AttnArgs a = attn_args(attn, layout, p);
+  set_order(a, attn, layout, p, true, kOrderRankMajor);
   a.lse_in = lse;
   a.partial = reinterpret_cast<float *>(workspace);
   const hipError_t e = launch_colscore(p, a, score, (hipStream_t)stream);

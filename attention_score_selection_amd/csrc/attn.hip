@@ -118,15 +118,16 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
-  const int hb = job / a.jobs_per_hb;
-  const int rj = job % a.jobs_per_hb;
   const int TB = a.TB;
-  int local;
-  const int seg = find_segment(a.nseg, rj, [&](int s) {
+  auto count = [&](int s) {
     int lo, hi;
     seg_tokens(a.L, a.segkind, s, lo, hi);
     return (hi - lo + TB - 1) / TB;
-  }, local);
+  };
+  int hb, rj;
+  job_order(a, job, hb, rj);
+  int local;
+  const int seg = find_segment(a.nseg, rj, count, local);
   if (seg < 0) return;
   int seg_lo, seg_hi;
   seg_tokens(a.L, a.segkind, seg, seg_lo, seg_hi);
@@ -220,16 +221,17 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
-  const int hb = job / a.jobs_per_hb;
-  const int rj = job % a.jobs_per_hb;
   const int KB = a.KB, RC = a.RC;
-  int local;
-  const int seg = find_segment(a.nseg, rj, [&](int s) {
+  auto count = [&](int s) {
     int lo, hi, sl, sh, cl, ch;
     seg_tokens(a.L, a.segkind, s, lo, hi);
     seg_images(a.L, a.segkind, s, sl, sh, cl, ch);
     return ((ch - cl + KB - 1) / KB) * ((hi - lo + RC - 1) / RC);
-  }, local);
+  };
+  int hb, rj;
+  job_order(a, job, hb, rj);
+  int local;
+  const int seg = find_segment(a.nseg, rj, count, local);
   if (seg < 0) return;
   int seg_lo, seg_hi, s_lo, s_hi, c_lo, c_hi;
   seg_tokens(a.L, a.segkind, seg, seg_lo, seg_hi);

@@ -130,15 +130,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs fa) {
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
-  const int hb = job / a.jobs_per_hb;
-  const int rj = job % a.jobs_per_hb;
   const int TB = a.TB;
-  int local;
-  const int seg = find_segment(a.nseg, rj, [&](int s) {
+  auto count = [&](int s) {
     int lo, hi;
     seg_tokens(a.L, a.segkind, s, lo, hi);
     return (hi - lo + TB - 1) / TB;
-  }, local);
+  };
+  int hb, rj;
+  job_order(a, job, hb, rj);
+  int local;
+  const int seg = find_segment(a.nseg, rj, count, local);
   if (seg < 0) return;
   int seg_lo, seg_hi;
   seg_tokens(a.L, a.segkind, seg, seg_lo, seg_hi);

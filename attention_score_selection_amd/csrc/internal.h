@@ -21,6 +21,12 @@ struct DevLayout {
 // or one per image (block-diagonal mask).
 enum SegKind { SEG_REQ = 0, SEG_IMG = 1 };
 
+// Order in which a launch runs the jobs of a head block (see job_order).  A
+// permutation travels in the kernel arguments, so launches with at most
+// kOrderMaxJobs jobs per head block can be reordered.
+enum JobOrder { kOrderPlain = 0, kOrderRankMajor = 1, kOrderSorted = 2 };
+constexpr int kOrderMaxJobs = 512;
+
 // Parameters of the LSE and column-score kernels.
 struct AttnArgs {
   DevLayout L;
@@ -37,6 +43,8 @@ struct AttnArgs {
   float c1;              // softmax scale * log2(e)
   int jobs_per_hb;       // jobs of one head block
   int total_jobs;        // nhb * jobs_per_hb
+  int order;             // JobOrder
+  unsigned perm[kOrderMaxJobs / 2];   // heaviest-first job permutation, 16 bits per entry (low half first)
   // LSE kernel
   float *lse_out;
   int TB;                // tokens per row block
