@@ -26,6 +26,10 @@ What it computes, and where the pages define it:
 * ``topk`` -- one global pool per request across all of its images
   (REDtech article, section 3.1 and 3.2), keeping the k largest scores; equal
   scores go to the lower candidate index; a non-finite score ranks as -inf.
+* ``mass_budget`` -- an input-dependent budget (a reading; the pages give
+  no algorithm): per pool the fewest top-ranked candidates whose score mass
+  reaches a fraction tau of the pool's total, clamped to [r_min, r_max] of
+  the pool, counted in integer mass units of 2^-32 so that k is exact.
 * ``compact`` / ``compact_loop`` -- stable compaction of each request: text
   tokens always stay, candidates stay iff kept; emits original packed token
   index, (image, row, col), new cu_seqlens and per-image kept counts, and the
@@ -333,6 +337,67 @@ def topk(prob, score: np.ndarray, ratios=None):
         key = np.where(np.isfinite(key), key, -np.inf)
         order = np.lexsort((np.arange(n), -key))
         keep[lo + order[:k]] = 1
+    return keep, np.asarray(ks, np.int64)
+
+
+def _ranked(score_pool) -> np.ndarray:
+    """Candidate order of one pool: largest score first, equal scores by lower
+    index, non-finite scores as -inf (the top-k order)."""
+    key = np.asarray(score_pool, np.float64)
+    key = np.where(np.isfinite(key), key, -np.inf)
+    return np.lexsort((np.arange(len(key)), -key))
+
+
+MASS_UNIT = 2.0 ** 32
+
+
+def mass_units(score_pool) -> np.ndarray:
+    """Score mass of each candidate in integer units of 2^-32:
+    floor(min(s, 1) * 2^32) for a finite s > 0, else 0.  (Scores are averages
+    of probabilities, so they lie in [0, 1]; integer units make the budget an
+    exact computation whatever the summation order.)"""
+    s = np.asarray(score_pool, np.float64)
+    ok = np.isfinite(s) & (s > 0)
+    return np.floor(np.minimum(np.where(ok, s, 0.0), 1.0) * MASS_UNIT).astype(np.uint64)
+
+
+def mass_budget_k(score_pool, tau: float, r_min: float, r_max: float) -> int:
+    """Input-dependent budget of one pool (a reading: the REDtech article,
+    section 6.2, lists choosing the compression rate from the input as future
+    work, and section 5.2 prunes less on detail-dense inputs; VisionZip's
+    observation, section 3.1, is that a few dominant tokens carry most of the
+    attention).  k* is the fewest top-ranked candidates whose mass reaches
+    target = min(M, ceil((tau * M) * (1 - 1e-12))) of the pool's total M (in
+    the units of ``mass_units``; products in binary64, the factor absorbing
+    the binary error of decimal fractions such as 0.9), then
+    k = clamp(k*, floor(r_min*N + 1e-6), floor(r_max*N + 1e-6))."""
+    for v in (tau, r_min, r_max):
+        if math.isnan(v):
+            raise ValueError("tau / r_min / r_max must not be NaN")
+    if r_min > r_max:
+        raise ValueError("r_min > r_max")
+    n = len(score_pool)
+    m = mass_units(score_pool)
+    total = int(m.sum(dtype=np.uint64))
+    t = min(max(float(tau), 0.0), 1.0)
+    target = min(total, int(math.ceil((t * float(total)) * (1.0 - 1e-12))))
+    if target == 0:
+        kstar = 0
+    else:
+        pref = np.cumsum(m[_ranked(score_pool)], dtype=np.uint64)
+        kstar = int(np.searchsorted(pref, np.uint64(target), side="left")) + 1
+    return min(max(kstar, budget_k(r_min, n)), budget_k(r_max, n))
+
+
+def mass_budget(prob, score: np.ndarray, tau, r_min, r_max):
+    """Keep flags (uint8 [N]) and k per pool under the input-dependent budget
+    (per-pool tau, r_min, r_max); the kept set is the top-k of ``topk``."""
+    keep = np.zeros(prob.N, np.uint8)
+    ks = []
+    for b, (lo, hi) in enumerate(pool_bounds(prob)):
+        k = mass_budget_k(score[lo:hi], tau[b], r_min[b], r_max[b])
+        ks.append(k)
+        keep[lo + _ranked(score[lo:hi])[:k]] = 1
     return keep, np.asarray(ks, np.int64)
 
 

@@ -495,6 +495,92 @@ def test_topk_k_zero_and_all_and_ties():
 
 
 # ---------------------------------------------------------------------------
+# Input-dependent (mass) budget.
+# ---------------------------------------------------------------------------
+
+def test_mass_units_hand_values():
+    sc = np.array([0.25, 1.0, 2.0, -1.0, np.nan, np.inf, 1e-12, 0.0, -0.0, 0.5 + 2.0 ** -40], np.float32)
+    m = oracle.mass_units(sc)
+    assert m.dtype == np.uint64
+    # 0.25 -> 2^30; 1 and 2 (clamped) -> 2^32; negative, NaN, inf, zeros -> 0;
+    # 1e-12 * 2^32 = 0.0043 -> 0; fp32 rounds 0.5 + 2^-40 to 0.5 -> 2^31.
+    assert list(m) == [2 ** 30, 2 ** 32, 2 ** 32, 0, 0, 0, 0, 0, 0, 2 ** 31]
+
+
+def _brute_kstar(sc, tau):
+    """Fewest candidates of ANY subset whose integer mass reaches the target
+    (the top-ranked subset of that size is the heaviest, so this equals k*)."""
+    m = [int(x) for x in oracle.mass_units(sc)]
+    total = sum(m)
+    target = min(total, math.ceil((tau * float(total)) * (1.0 - 1e-12)))
+    if target == 0:
+        return 0
+    n = len(m)
+    for size in range(1, n + 1):
+        for mask in range(1 << n):
+            if bin(mask).count("1") == size and sum(m[i] for i in range(n) if mask >> i & 1) >= target:
+                return size
+    raise AssertionError("target above total")
+
+
+def test_mass_budget_matches_subset_brute_force():
+    rng = np.random.default_rng(21)
+    for trial in range(60):
+        n = int(rng.integers(1, 9))
+        sc = (rng.integers(0, 6, size=n) / rng.integers(5, 40)).astype(np.float32)
+        if trial % 7 == 3:
+            sc[rng.integers(0, n)] = np.nan
+        if trial % 11 == 5:
+            sc[rng.integers(0, n)] = -0.5
+        tau = float(rng.choice([0.0, 0.1, 0.25, 0.5, 0.6, 0.9, 0.999, 1.0, rng.random()]))
+        k = oracle.mass_budget_k(sc, tau, 0.0, 1.0)
+        assert k == _brute_kstar(sc, tau), (sc, tau)
+
+
+def test_mass_budget_uniform_closed_form():
+    # n equal scores: k* = tau * n exactly for decimal tau on the grid 1/n.
+    for n in (4, 10, 20, 100):
+        sc = np.full(n, 1.0 / n, np.float32)
+        for i in range(n + 1):
+            assert oracle.mass_budget_k(sc, i / n, 0.0, 1.0) == i, (n, i)
+
+
+def test_mass_budget_dominant_and_edges():
+    sc = np.array([0.01] * 5 + [0.9] + [0.01] * 5, np.float32)
+    assert oracle.mass_budget_k(sc, 0.5, 0.0, 1.0) == 1  # the dominant token alone
+    assert oracle.mass_budget_k(sc, 0.0, 0.0, 1.0) == 0
+    assert oracle.mass_budget_k(sc, 1.0, 0.0, 1.0) == 11  # every positive-mass candidate
+    assert oracle.mass_budget_k(sc, 0.5, 0.4, 1.0) == 4  # floor(0.4 * 11) lower bound
+    assert oracle.mass_budget_k(sc, 1.0, 0.0, 0.5) == 5  # floor(0.5 * 11) upper bound
+    zero = np.zeros(7, np.float32)
+    assert oracle.mass_budget_k(zero, 0.9, 0.0, 1.0) == 0  # no mass: nothing needed
+    assert oracle.mass_budget_k(zero, 0.9, 0.3, 1.0) == 2
+    assert oracle.mass_budget_k(np.zeros(0, np.float32), 0.5, 0.0, 1.0) == 0
+    with_zero = np.array([0.5, 0.0, 0.25, 0.0], np.float32)
+    assert oracle.mass_budget_k(with_zero, 1.0, 0.0, 1.0) == 2  # zero-mass candidates never needed
+    for bad in [(float("nan"), 0.0, 1.0), (0.5, float("nan"), 1.0), (0.5, 0.6, 0.5)]:
+        with pytest.raises(ValueError):
+            oracle.mass_budget_k(sc, *bad)
+
+
+def test_mass_budget_monotone_and_keeps_top_k():
+    rng = np.random.default_rng(22)
+    p = random_small(22, "full", dtype="f32", n_req=3)
+    sc = rng.gamma(0.5, size=p.N) / p.N
+    sc[::9] = sc[1::9]  # some exact ties
+    prev = None
+    for tau in np.linspace(0.0, 1.0, 21):
+        keep, ks = oracle.mass_budget(p, sc, [tau] * p.B, [0.1] * p.B, [0.95] * p.B)
+        for b, (lo, hi) in enumerate(oracle.pool_bounds(p)):
+            n = hi - lo
+            assert oracle.budget_k(0.1, n) <= ks[b] <= oracle.budget_k(0.95, n)
+            np.testing.assert_array_equal(keep[lo:hi], brute_keep(sc[lo:hi], ks[b]))
+        if prev is not None:
+            assert (ks >= prev).all()
+        prev = ks
+
+
+# ---------------------------------------------------------------------------
 # Compaction.
 # ---------------------------------------------------------------------------
 
