@@ -21,7 +21,7 @@ TSEL_F32, TSEL_F16, TSEL_BF16, TSEL_FP8_E4M3 = 0, 1, 2, 3
 MASKS = {"full": 0, "causal": 1, "blockdiag": 2}
 TSEL_OP_LSE, TSEL_OP_COLSCORE, TSEL_OP_TOPK, TSEL_OP_COMPACT, TSEL_OP_MROPE = 0, 1, 2, 3, 4
 EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact", "tsel_mrope_positions",
-           "tsel_attention_fwd",
+           "tsel_attention_fwd", "tsel_budget_mass",
            "tsel_workspace_size", "tsel_last_error", "tsel_version")
 
 _DTYPES = {torch.float32: TSEL_F32, torch.float16: TSEL_F16, torch.bfloat16: TSEL_BF16,
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_size_t, _P]
         L.tsel_budget_topk.restype = ctypes.c_int
         L.tsel_budget_topk.argtypes = [ctypes.POINTER(CLayout), _P, _P, _P, _P, _P]
+        L.tsel_budget_mass.restype = ctypes.c_int
+        L.tsel_budget_mass.argtypes = [ctypes.POINTER(CLayout), _P, _P, _P, _P, _P, _P, _P]
         L.tsel_compact.restype = ctypes.c_int
         L.tsel_compact.argtypes = [ctypes.POINTER(CLayout), _P, _P, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P, _P, _P,
@@ -206,6 +208,23 @@ def tsel_budget_topk(layout: Layout, score: torch.Tensor, keep_ratio: Sequence[f
     _check(lib().tsel_budget_topk(ctypes.byref(layout.c), _ptr(score), ratios.ctypes.data,
                                   k_h.ctypes.data, _ptr(out), _stream(score.device)))
     return out, k_h
+
+
+def tsel_budget_mass(layout: Layout, score: torch.Tensor, tau: Sequence[float], r_min: Sequence[float],
+                     r_max: Sequence[float], out: Optional[torch.Tensor] = None,
+                     k_out: Optional[torch.Tensor] = None):
+    """Input-dependent budget: keep flags (uint8 [N]) and k per pool (device
+    int32 [B]; ``.cpu()`` it to size the compaction)."""
+    arrs = [np.ascontiguousarray(np.asarray(x, np.float64).reshape(-1)) for x in (tau, r_min, r_max)]
+    if any(a.size != layout.B for a in arrs):
+        raise ValueError("one tau, r_min and r_max per request are required")
+    if out is None:
+        out = torch.empty((layout.N,), dtype=torch.uint8, device=score.device)
+    if k_out is None:
+        k_out = torch.empty((max(layout.B, 1),), dtype=torch.int32, device=score.device)
+    _check(lib().tsel_budget_mass(ctypes.byref(layout.c), _ptr(score), arrs[0].ctypes.data, arrs[1].ctypes.data,
+                                  arrs[2].ctypes.data, _ptr(k_out), _ptr(out), _stream(score.device)))
+    return out, k_out[:layout.B]
 
 
 def tsel_compact(layout: Layout, keep: torch.Tensor, k_per_pool, emb: Optional[torch.Tensor] = None,

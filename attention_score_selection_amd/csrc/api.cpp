@@ -448,6 +448,46 @@ int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const doub
   return TSEL_OK;
 }
 
+int tsel_budget_mass(const tsel_layout_t *layout, const float *score, const double *tau_h,
+                     const double *r_min_h, const double *r_max_h, int32_t *k, uint8_t *keep,
+                     void *stream) {
+  clear_error();
+  int rc = check_layout(layout);
+  if (rc != TSEL_OK) return rc;
+  const int B = layout->num_reqs;
+  if (tau_h == nullptr || r_min_h == nullptr || r_max_h == nullptr)
+    return fail(TSEL_EINVAL, "tau_h, r_min_h and r_max_h are required");
+  if (k == nullptr || ((uintptr_t)k & 3)) return fail(TSEL_EINVAL, "k must be a 4-byte aligned device array");
+  const int N = layout->cu_cands_h[layout->num_images];
+  if (N > 0 && (score == nullptr || keep == nullptr)) return fail(TSEL_EINVAL, "score and keep are required");
+  auto clamp01 = [](double v) { return std::min(1.0, std::max(0.0, v)); };
+  for (int b = 0; b < B; ++b) {
+    if (isnan(tau_h[b]) || isnan(r_min_h[b]) || isnan(r_max_h[b]))
+      return fail(TSEL_EINVAL, "tau/r_min/r_max of pool %d is NaN", b);
+    if (clamp01(r_min_h[b]) > clamp01(r_max_h[b])) return fail(TSEL_EINVAL, "r_min > r_max in pool %d", b);
+  }
+  const DevLayout L = dev_layout(layout);
+  for (int b0 = 0; b0 < B; b0 += kMassChunk) {
+    MassChunk mc{};
+    mc.b0 = b0;
+    const int np = std::min(kMassChunk, B - b0);
+    for (int i = 0; i < np; ++i) {
+      const int b = b0 + i;
+      const long long nb = layout->cu_cands_h[layout->cu_images_h[b + 1]] -
+                           layout->cu_cands_h[layout->cu_images_h[b]];
+      auto bound = [&](double r) {
+        return (int)std::min(nb, std::max(0LL, (long long)floor(clamp01(r) * (double)nb + 1e-6)));
+      };
+      mc.kmin[i] = bound(r_min_h[b]);
+      mc.kmax[i] = bound(r_max_h[b]);
+      mc.tau[i] = clamp01(tau_h[b]);
+    }
+    const hipError_t e = launch_mass_budget(L, score, mc, np, k, keep, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_budget_mass launch: %s", hipGetErrorString(e));
+  }
+  return TSEL_OK;
+}
+
 int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *emb,
                  int64_t emb_stride, int64_t emb_row_bytes, int32_t out_capacity, void *out_emb,
                  int64_t out_emb_stride, int32_t *out_token_idx, int32_t *out_spatial,

@@ -92,6 +92,17 @@ struct TopkChunk {
 hipError_t launch_topk(const DevLayout &L, const float *score, const TopkChunk &ks, int npools,
                        uint8_t *keep, hipStream_t s);
 
+// Input-dependent budget: per-pool target fraction and k bounds (64 pools a launch).
+constexpr int kMassChunk = 64;
+struct MassChunk {
+  int b0;                 // first pool of this launch
+  int kmin[kMassChunk];   // floor(r_min * N_b + 1e-6)
+  int kmax[kMassChunk];   // floor(r_max * N_b + 1e-6)
+  double tau[kMassChunk];  // target fraction of the pool's mass, in [0, 1]
+};
+hipError_t launch_mass_budget(const DevLayout &L, const float *score, const MassChunk &mc, int npools,
+                              int *k_out, uint8_t *keep, hipStream_t s);
+
 struct CompactArgs {
   DevLayout L;
   const uint8_t *keep;

@@ -6,7 +6,10 @@
 // LDS histograms), which yields the k-th largest key tau and how many keys
 // equal to tau still fit; a block-wide ordered scan then admits those equal
 // keys by ascending candidate index.  No floating-point atomics: the result
-// is exact and deterministic.
+// is exact and deterministic.  The input-dependent budget reuses that
+// descent with integer mass histograms to find how many candidates a pool
+// keeps (the REDtech article's section 6.2 names choosing the rate from the
+// input; the mass-coverage rule is this library's reading).
 //
 // Compaction (new lengths, image boundaries and original spatial indices,
 // REDtech article section 3.2): per-block keep counts, one scan block, then a
@@ -61,17 +64,21 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total) {
 // counts.
 constexpr int kTopkRegKeys = 32;
 
+// known: tau = `known_tau` and `known_kr` keys equal to it are kept (the
+// caller found them already); the descent is skipped.
 __device__ __forceinline__ void topk_registers(const float *score, int n, int k, uint8_t *keep,
-                                               int *hist, int *sh, int &s_digit, int &s_above) {
+                                               int *hist, int *sh, int &s_digit, int &s_above,
+                                               bool known = false, uint32_t known_tau = 0u,
+                                               int known_kr = 0) {
   const int tid = threadIdx.x;
   const int per = (n + kTopkThreads - 1) / kTopkThreads;
   const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
   uint32_t u[kTopkRegKeys];
 #pragma unroll
   for (int j = 0; j < kTopkRegKeys; ++j) u[j] = (i0 + j < i1) ? score_key(score[i0 + j]) : 0u;
-  uint32_t prefix = 0u, pmask = 0u;
-  int kr = k;  // how many of the keys matching `prefix` must still be kept
-  for (int pass = 0; pass < 4; ++pass) {
+  uint32_t prefix = known ? known_tau : 0u, pmask = 0u;
+  int kr = known ? known_kr : k;  // how many of the keys matching `prefix` must still be kept
+  for (int pass = 0; pass < (known ? 0 : 4); ++pass) {
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
@@ -123,35 +130,29 @@ __device__ __forceinline__ void topk_registers(const float *score, int n, int k,
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const float *score,
-                                                           TopkChunk ks, uint8_t *keep) {
-  __shared__ int hist[256];
-  __shared__ int sh[17];
-  __shared__ int s_digit, s_above;
-  const int b = ks.b0 + blockIdx.x;
-  const int lo = L.cu_cands[L.cu_images[b]];
-  const int hi = L.cu_cands[L.cu_images[b + 1]];
-  const int n = hi - lo;
-  const int k = ks.k[blockIdx.x];
+// Keep flags of one pool of n candidates: the k largest keys, equal keys by
+// ascending index.  Every thread of the 1024-thread block calls it.
+__device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint8_t *keep, int *hist, int *sh, int &s_digit,
+                          int &s_above, bool known = false, uint32_t known_tau = 0u, int known_kr = 0) {
   const int tid = threadIdx.x;
   if (n <= 0) return;
   if (k <= 0 || k >= n) {
     const uint8_t f = (k >= n) ? 1 : 0;
-    for (int i = tid; i < n; i += kTopkThreads) keep[lo + i] = f;
+    for (int i = tid; i < n; i += kTopkThreads) keep[i] = f;
     return;
   }
   if (n <= kTopkThreads * kTopkRegKeys) {
-    topk_registers(score + lo, n, k, keep + lo, hist, sh, s_digit, s_above);
+    topk_registers(score, n, k, keep, hist, sh, s_digit, s_above, known, known_tau, known_kr);
     return;
   }
-  uint32_t prefix = 0u, pmask = 0u;
-  int kr = k;  // how many of the keys matching `prefix` must still be kept
-  for (int pass = 0; pass < 4; ++pass) {
+  uint32_t prefix = known ? known_tau : 0u, pmask = 0u;
+  int kr = known ? known_kr : k;  // how many of the keys matching `prefix` must still be kept
+  for (int pass = 0; pass < (known ? 0 : 4); ++pass) {
     const int shift = 24 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kTopkThreads) {
-      const uint32_t u = score_key(score[lo + i]);
+      const uint32_t u = score_key(score[i]);
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
     }
     __syncthreads();
@@ -178,13 +179,209 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const f
   int seen = 0;
   for (int base = 0; base < n; base += kTopkThreads) {
     const int i = base + tid;
-    const uint32_t u = (i < n) ? score_key(score[lo + i]) : 0u;
+    const uint32_t u = (i < n) ? score_key(score[i]) : 0u;
     const int eq = (i < n && u == prefix) ? 1 : 0;
     int tot;
     const int rank = block_excl_scan(eq, sh, tot) + seen;
-    if (i < n) keep[lo + i] = (u > prefix || (eq && rank < kr)) ? 1 : 0;
+    if (i < n) keep[i] = (u > prefix || (eq && rank < kr)) ? 1 : 0;
     seen += tot;
   }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const float *score,
+                                                           TopkChunk ks, uint8_t *keep) {
+  __shared__ int hist[256];
+  __shared__ int sh[17];
+  __shared__ int s_digit, s_above;
+  const int b = ks.b0 + blockIdx.x;
+  const int lo = L.cu_cands[L.cu_images[b]];
+  const int hi = L.cu_cands[L.cu_images[b + 1]];
+  topk_pool(score + lo, hi - lo, ks.k[blockIdx.x], keep + lo, hist, sh, s_digit, s_above);
+}
+
+// ---------------------------------------------------------------------------
+// Input-dependent budget.  Mass of a candidate in integer units of 2^-32:
+// floor(min(s, 1) * 2^32) for a finite s > 0, else 0; mass never decreases
+// with the score, so the candidates ranked first are the heaviest.  Per pool:
+// total M, target = min(M, ceil((tau * M) * (1 - 1e-12))) in binary64, and
+// k* = fewest top-ranked candidates whose mass reaches the target, found by
+// the same MSB-first radix descent as the top-k with per-digit mass (64-bit
+// integer) as well as count histograms: the descent stops at the key whose
+// candidates (all of one mass m*) complete the target, k* = (candidates
+// above it) + ceil(remaining / m*).  Integer sums make k* independent of the
+// summation order.
+// ---------------------------------------------------------------------------
+// Mass of the candidate whose order key is u, in integer arithmetic on the
+// float's bits: a finite positive score s = man * 2^(ex - 150) (ex the biased
+// exponent, man the 24-bit significand) has floor(s * 2^32) = man shifted by
+// ex - 118; s >= 1 clamps to 2^32; non-finite, zero and negative scores (keys
+// at or below 0x80000000) carry none.
+__device__ __forceinline__ unsigned long long key_mass(uint32_t u) {
+  if (u <= 0x80000000u) return 0ull;
+  const uint32_t bits = u & 0x7fffffffu;
+  if (bits >= 0x3f800000u) return 1ull << 32;
+  const int ex = (int)(bits >> 23);
+  if (ex < 95) return 0ull;  // s < 2^-32 (subnormals included)
+  const uint32_t man = (bits & 0x7fffffu) | 0x800000u;
+  const int sh = ex - 118;
+  return (unsigned long long)(sh >= 0 ? (man << sh) : (man >> (-sh)));
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, const float *score, MassChunk mc,
+                                                                  int *k_out, uint8_t *keep) {
+  __shared__ int hist[256];
+  __shared__ int sh[17];
+  __shared__ int s_digit, s_above;
+  __shared__ unsigned long long hmass[256];
+  __shared__ unsigned long long s_target, s_mabove;
+  __shared__ int s_k;
+  const int b = mc.b0 + blockIdx.x;
+  const int lo = L.cu_cands[L.cu_images[b]];
+  const int n = L.cu_cands[L.cu_images[b + 1]] - lo;
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
+  const float *sc = score + lo;
+  // Pools of up to kTopkThreads * kTopkRegKeys candidates keep their keys in
+  // registers, a contiguous run per thread, and merge histogram adds while
+  // consecutive keys share a digit (the leading digits of a pool's scores
+  // are mostly equal, so unmerged adds would serialise on one address).
+  const bool regs = n <= kTopkThreads * kTopkRegKeys;
+  const int per = (n + kTopkThreads - 1) / kTopkThreads;
+  const int i0 = regs ? min(n, tid * per) : 0, i1 = regs ? min(n, i0 + per) : 0;
+  uint32_t u[kTopkRegKeys];
+#pragma unroll
+  for (int j = 0; j < kTopkRegKeys; ++j) u[j] = (i0 + j < i1) ? score_key(sc[i0 + j]) : 0u;
+
+  uint32_t prefix = 0u, pmask = 0u;
+  unsigned long long R = 0ull;  // mass still to cover among keys matching `prefix`
+  unsigned long long mstar = 0ull;
+  int kstar = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) {
+      hist[tid] = 0;
+      hmass[tid] = 0ull;
+    }
+    __syncthreads();
+    if (regs) {
+      // (Recompute the masses every pass: kept across passes they would take
+      // 64 more registers per thread.)
+#pragma unroll
+      for (int j = 0; j < kTopkRegKeys; ++j) asm volatile("" : "+v"(u[j]));
+      int cur = -1, cnt = 0;
+      unsigned long long ms = 0ull;
+#pragma unroll
+      for (int j = 0; j < kTopkRegKeys; ++j) {
+        if (i0 + j < i1 && (u[j] & pmask) == prefix) {
+          const int d = (int)((u[j] >> shift) & 255u);
+          if (d != cur) {
+            if (cnt) {
+              atomicAdd(&hist[cur], cnt);
+              if (ms) atomicAdd(&hmass[cur], ms);
+            }
+            cur = d;
+            cnt = 0;
+            ms = 0ull;
+          }
+          ++cnt;
+          ms += key_mass(u[j]);
+        }
+      }
+      if (cnt) {
+        atomicAdd(&hist[cur], cnt);
+        if (ms) atomicAdd(&hmass[cur], ms);
+      }
+    } else {
+      for (int i = tid; i < n; i += kTopkThreads) {
+        const uint32_t v = score_key(sc[i]);
+        if ((v & pmask) == prefix) {
+          const int d = (int)((v >> shift) & 255u);
+          atomicAdd(&hist[d], 1);
+          const unsigned long long m = key_mass(v);
+          if (m) atomicAdd(&hmass[d], m);
+        }
+      }
+    }
+    __syncthreads();
+    if (pass == 0) {
+      // The first histogram covers the whole pool: total mass and target.
+      if (tid == 0) {
+        unsigned long long total = 0ull;
+        for (int d = 0; d < 256; ++d) total += hmass[d];
+        const double x = ceil((mc.tau[blockIdx.x] * (double)total) * (1.0 - 1e-12));
+        const unsigned long long tg = (unsigned long long)x;
+        s_target = tg < total ? tg : total;
+      }
+      __syncthreads();
+      R = s_target;
+      if (R == 0ull) break;  // uniform across the block
+    }
+    // Wave 0 walks the digits from 255 down: lane l holds digits 255-4l .. 252-4l.
+    if (wid == 0) {
+      unsigned long long msum = 0ull;
+      int csum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        msum += hmass[255 - 4 * lane - j];
+        csum += hist[255 - 4 * lane - j];
+      }
+      unsigned long long mb = wave_incl_scan_u64(msum) - msum;  // mass of larger digits
+      int cb = wave_incl_scan(csum) - csum;                    // count of larger digits
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned long long mj = hmass[255 - 4 * lane - j];
+        if (mb < R && mb + mj >= R) {
+          s_digit = 255 - 4 * lane - j;
+          s_above = cb;
+          s_mabove = mb;
+        }
+        mb += mj;
+        cb += hist[255 - 4 * lane - j];
+      }
+    }
+    __syncthreads();
+    const int d = s_digit;
+    R -= s_mabove;
+    kstar += s_above;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
+    if (pass == 3) mstar = hmass[d] / (unsigned long long)hist[d];  // one key: one mass
+    __syncthreads();
+  }
+  // R > 0 here only if the descent ran: the candidates of key `prefix` (each
+  // of mass mstar) complete the target, and the k*-th largest key is
+  // `prefix` itself, with `need` of its candidates kept.
+  int need = 0;
+  if (R > 0ull) {
+    need = (int)((R + mstar - 1ull) / mstar);
+    kstar += need;
+  }
+  if (tid == 0) {
+    const int k = min(max(kstar, mc.kmin[blockIdx.x]), mc.kmax[blockIdx.x]);
+    s_k = k;
+    k_out[b] = k;
+  }
+  __syncthreads();
+  const int k = s_k;
+  // Unclamped and inside the pool: reuse the threshold; otherwise select anew.
+  const bool known = need > 0 && k == kstar && k < n;
+  topk_pool(sc, n, k, keep + lo, hist, sh, s_digit, s_above, known, prefix, need);
 }
 
 // Keep decision of token t: text tokens stay, candidates follow their flag.
@@ -361,6 +558,13 @@ hipError_t launch_topk(const DevLayout &L, const float *score, const TopkChunk &
                        uint8_t *keep, hipStream_t s) {
   if (npools <= 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3(npools), dim3(kTopkThreads), 0, s, L, score, ks, keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_mass_budget(const DevLayout &L, const float *score, const MassChunk &mc, int npools,
+                              int *k_out, uint8_t *keep, hipStream_t s) {
+  if (npools <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mass_budget_kernel, dim3(npools), dim3(kTopkThreads), 0, s, L, score, mc, k_out, keep);
   return hipGetLastError();
 }
 

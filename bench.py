@@ -124,6 +124,30 @@ def time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems):
             "flops_per_launch": flops}
 
 
+def time_mass(tsel, prob, score, lay, dev, stream, args):
+    """tsel_budget_mass on the step's own scores (target fraction --mass-tau,
+    bounds [0, 1]) timed with HIP events; algorithmic bytes 5 per candidate
+    (score read, flag written), as for the top-k."""
+    import torch
+    B = prob.B
+    tau, lo, hi = [args.mass_tau] * B, [0.0] * B, [1.0] * B
+    keep = torch.empty((prob.N,), dtype=torch.uint8, device=dev)
+    kd = torch.empty((max(B, 1),), dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        tsel.tsel_budget_mass(lay, score, tau, lo, hi, out=keep, k_out=kd)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        tsel.tsel_budget_mass(lay, score, tau, lo, hi, out=keep, k_out=kd)
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    t = ev[0].elapsed_time(ev[1]) / 1e3 / args.steps
+    ks = [int(x) for x in kd[:B].cpu()]
+    return {"ms": t * 1e3, "tau": args.mass_tau, "k": ks if B > 1 else ks[0],
+            "kept_fraction": sum(ks) / max(prob.N, 1), "candidates_per_s": prob.N / t,
+            "GBps": 5.0 * prob.N / t / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +158,8 @@ def main():
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
     ap.add_argument("--forward", action="store_true",
                     help="also time the attention forward (tsel_attention_fwd) on the same layer")
+    ap.add_argument("--mass-tau", type=float, default=None,
+                    help="also time the input-dependent budget (tsel_budget_mass) at this mass fraction")
     ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=4,
                     help="named workload (default 4: the 16384-token GQA decoder layer); the others are "
                          "parity workloads, timed here for reference only")
@@ -254,6 +280,8 @@ def main():
     }
     if args.forward:
         result["attention_forward"] = time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems)
+    if args.mass_tau is not None:
+        result["budget_mass"] = time_mass(tsel, prob, score, lay, dev, stream, args)
     if args.calib_copy_mb > 0:
         n = args.calib_copy_mb << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)

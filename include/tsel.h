@@ -12,7 +12,9 @@
  *   tsel_budget_topk  one top-k per request pool, k = floor(r * N + 1e-6)
  *   tsel_compact      stable compaction and gather of the kept tokens
  *
- * and two calls sit on either side of it:
+ * tsel_budget_mass replaces the fixed ratio of tsel_budget_topk with a budget
+ * read from the scores themselves, and two calls sit on either side of the
+ * path:
  *
  *   tsel_attention_fwd    the layer's attention forward, which yields the LSE
  *                         the selection can reuse instead of tsel_lse
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define TSEL_VERSION 2
+#define TSEL_VERSION 3
 
 #define TSEL_OK 0
 #define TSEL_EINVAL (-1)      /* bad pointer, size, offset, ratio or layout        */
@@ -161,6 +163,27 @@ int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const fl
  * synchronously.  keep: device uint8 [N], 1 = kept.  No workspace. */
 int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const double *keep_ratio_h,
                      int32_t *k_h, uint8_t *keep, void *stream);
+
+/* Input-dependent budget (the REDtech article, section 6.2, names choosing
+ * the compression rate from the input as the next step and gives no rule;
+ * section 5.2 prunes less on detail-dense inputs, and section 3.1's premise is
+ * that a few dominant tokens gather most of the attention; this call is this
+ * library's reading).  Scores are read as attention mass, in integer units of
+ * 2^-32: m = floor(min(s, 1) * 2^32) for a finite s > 0, else 0.  For pool b
+ * with total mass M_b (exact 64-bit sum),
+ *   target = min(M_b, ceil((tau_b * M_b) * (1 - 1e-12)))         (binary64)
+ *   k*_b   = fewest candidates, taken in the tsel_budget_topk order, whose
+ *            mass reaches target (0 when target is 0)
+ *   k_b    = clamp(k*_b, floor(r_min_b * N_b + 1e-6), floor(r_max_b * N_b + 1e-6))
+ * and the k_b candidates are kept exactly as tsel_budget_topk keeps them.  A
+ * pool whose attention concentrates on a few tokens keeps few; a diffuse one
+ * keeps many.  tau_h, r_min_h, r_max_h: host [B], clamped to [0, 1]; NaN or
+ * r_min > r_max is TSEL_EINVAL.  k: device int32 [B], written on `stream`
+ * (tsel_compact needs the kept counts only through `keep`; copy k to the host
+ * to size its outputs exactly).  keep: device uint8 [N].  No workspace. */
+int tsel_budget_mass(const tsel_layout_t *layout, const float *score, const double *tau_h,
+                     const double *r_min_h, const double *r_max_h, int32_t *k, uint8_t *keep,
+                     void *stream);
 
 /* Stable compaction of every request (REDtech article, section 3.2: new
  * multimodal lengths, image boundaries and original spatial indices).  A

@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_path(lib):
     names = declared_functions()
     for n in ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact", "tsel_attention_fwd",
-              "tsel_mrope_positions"):
+              "tsel_mrope_positions", "tsel_budget_mass"):
         assert n in names
     assert set(names) == set(B.EXPORTS)
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version(lib):
     header = open(HEADER).read()
     want = int(re.search(r"#define TSEL_VERSION (\d+)", header).group(1))
-    assert lib.tsel_version() == want == 2
+    assert lib.tsel_version() == want == 3
 
 
 FAKE = 4096  # non-null device address that validation never dereferences
@@ -147,6 +147,21 @@ def test_topk_rejects_nan_ratio(lib):
     k_h = np.zeros(2, np.int32)
     rc = lib.tsel_budget_topk(ctypes.byref(lay.c), FAKE, ratios.ctypes.data, k_h.ctypes.data, FAKE, None)
     assert rc == B.TSEL_EINVAL and "NaN" in last_error(lib)
+
+
+@pytest.mark.parametrize("tau,rmin,rmax,msg", [((0.5, np.nan), (0.0, 0.0), (1.0, 1.0), "NaN"),
+                                                ((0.5, 0.5), (0.0, np.nan), (1.0, 1.0), "NaN"),
+                                                ((0.5, 0.5), (0.0, 0.7), (1.0, 0.6), "r_min > r_max")])
+def test_budget_mass_validation(lib, tau, rmin, rmax, msg):
+    """Bad host arguments fail before any launch (no GPU needed)."""
+    lay = good_layout()
+    arrs = [np.asarray(x, np.float64) for x in (tau, rmin, rmax)]
+    rc = lib.tsel_budget_mass(ctypes.byref(lay.c), FAKE, arrs[0].ctypes.data, arrs[1].ctypes.data,
+                              arrs[2].ctypes.data, FAKE, FAKE, None)
+    assert rc == B.TSEL_EINVAL and msg in last_error(lib)
+    rc = lib.tsel_budget_mass(ctypes.byref(lay.c), FAKE, arrs[0].ctypes.data, arrs[1].ctypes.data,
+                              None, FAKE, FAKE, None)
+    assert rc == B.TSEL_EINVAL
 
 
 def test_workspace_sizes_and_shortfall(lib):
