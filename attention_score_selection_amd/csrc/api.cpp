@@ -65,8 +65,8 @@ static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
   if (a->dtype != TSEL_F32 && a->dtype != TSEL_F16 && a->dtype != TSEL_BF16 &&
       a->dtype != TSEL_FP8_E4M3)
     return fail(TSEL_EUNSUPPORTED, "dtype %d is not supported", (int)a->dtype);
-  if (a->head_dim != 64 && a->head_dim != 80 && a->head_dim != 96 && a->head_dim != 128)
-    return fail(TSEL_EUNSUPPORTED, "head_dim %d is not one of 64, 80, 96, 128", a->head_dim);
+  if (a->head_dim != 64 && a->head_dim != 72 && a->head_dim != 80 && a->head_dim != 96 && a->head_dim != 128)
+    return fail(TSEL_EUNSUPPORTED, "head_dim %d is not one of 64, 72, 80, 96, 128", a->head_dim);
   if (a->dtype == TSEL_FP8_E4M3 && a->head_dim != 64 && a->head_dim != 128)
     return fail(TSEL_EUNSUPPORTED, "fp8 inputs need head_dim 64 or 128 (got %d)", a->head_dim);
   if (a->num_heads_q < 1 || a->num_heads_kv < 1 || a->num_heads_q % a->num_heads_kv != 0)

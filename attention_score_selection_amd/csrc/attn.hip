@@ -45,7 +45,7 @@ namespace tsel {
 template <int DT, int D, int NG, bool MAXMODE>
 __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, int key_lo,
                                          int key_hi, int t0, int t1,
-                                         const Chunk<DT> (&qf)[NG][D / Elem<DT>::KW],
+                                         const Chunk<DT> (&qf)[NG][kch(DT, D)],
                                          const int (&qtok)[NG],
                                          int wtok_min, int wtok_max, const float (&m)[NG],
                                          float (&acc)[NG]) {
@@ -477,6 +477,7 @@ hipError_t lse_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   } else {
     switch (p.D) {
       case 64: return lse_ng<DT, 64>(p, a, s);
+      case 72: return lse_ng<DT, 72>(p, a, s);
       case 80: return lse_ng<DT, 80>(p, a, s);
       case 96: return lse_ng<DT, 96>(p, a, s);
       default: return lse_ng<DT, 128>(p, a, s);
@@ -490,6 +491,7 @@ hipError_t col_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
   } else {
     switch (p.D) {
       case 64: return col_ng<DT, 64>(p, a, s);
+      case 72: return col_ng<DT, 72>(p, a, s);
       case 80: return col_ng<DT, 80>(p, a, s);
       case 96: return col_ng<DT, 96>(p, a, s);
       default: return col_ng<DT, 128>(p, a, s);

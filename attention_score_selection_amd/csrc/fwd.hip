@@ -303,6 +303,7 @@ template <int DT>
 hipError_t fwd_d(const AttnPlan &p, const FwdArgs &a, hipStream_t s) {
   switch (p.D) {
     case 64: return fwd_go<DT, 64>(p, a, s);
+    case 72: return fwd_go<DT, 72>(p, a, s);
     case 80: return fwd_go<DT, 80>(p, a, s);
     case 96: return fwd_go<DT, 96>(p, a, s);
     default: return fwd_go<DT, 128>(p, a, s);

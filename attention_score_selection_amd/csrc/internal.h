@@ -132,7 +132,8 @@ constexpr int kBufferLimit = 0x7FFFFFF0;
 // per SIMD).
 constexpr int max_groups(int dtype, int head_dim) {
   const int es = dtype == TSEL_F32 ? 4 : dtype == TSEL_FP8_E4M3 ? 1 : 2;
-  const int per_group = head_dim * es / 8;  // VGPRs
+  const int kw = dtype == TSEL_FP8_E4M3 ? 64 : 16;
+  const int per_group = (head_dim + kw - 1) / kw * kw * es / 8;  // VGPRs (padded k)
   return per_group <= 20 ? 4 : per_group <= 32 ? 3 : per_group <= 48 ? 2 : 1;
 }
 

@@ -97,15 +97,26 @@ __device__ __forceinline__ f32x16 mma<TSEL_FP8_E4M3>(const Chunk<TSEL_FP8_E4M3> 
 
 constexpr int kRows = 32;  // rows of a streamed tile and of a resident group
 
-// Geometry of one streamed 32-row tile in LDS.
+// k chunks of a head dim (rounded up to whole chunks).
+constexpr int kch(int dt, int d) {
+  const int kw = dt == TSEL_FP8_E4M3 ? 64 : 16;
+  return (d + kw - 1) / kw;
+}
+
+// Geometry of one streamed 32-row tile in LDS.  A head dim that is not a
+// multiple of the k width (72 for 16-bit types) is padded with zeros to the
+// next one: the padded units are staged as zeros and the padded k values of
+// the resident operand are zero, so they add nothing to the contraction.
 template <int DT, int D>
 struct Geom {
+  static_assert((D * Elem<DT>::ES) % 16 == 0, "a row must be whole 16-byte units");
   static constexpr int ES = Elem<DT>::ES;
   static constexpr int KW = Elem<DT>::KW;
-  static constexpr int KCH = D / KW;                   // KW-wide k chunks (one MFMA step each)
-  static constexpr int ROW = D * ES;                   // bytes of a row
+  static constexpr int KCH = kch(DT, D);               // KW-wide k chunks (one MFMA step each)
+  static constexpr int ROW = KCH * KW * ES;            // bytes of a (padded) row in LDS
   static constexpr int RS = ROW + 16;                  // LDS row stride (bank spread)
-  static constexpr int UNITS = ROW / 16;               // 16-byte units per row
+  static constexpr int UNITS = ROW / 16;               // 16-byte units per (padded) row
+  static constexpr int UNITS_D = D * ES / 16;          // ... of which hold data
   static constexpr int UPT = (kRows * UNITS + 255) / 256;  // units per thread (256 threads)
   // LDS tile: 16-byte slots, UNITS + 1 per row (the last pads the row), the
   // slot count rounded up to whole 64-slot blocks (one wave's direct load).
@@ -148,7 +159,7 @@ struct StageRegs {
       const int u = threadIdx.x + 256 * i;
       if (u < kRows * G::UNITS) {
         row[i] = u / G::UNITS;
-        off[i] = rowoff(row[i]) + (u % G::UNITS) * 16;
+        off[i] = (u % G::UNITS < G::UNITS_D) ? rowoff(row[i]) + (u % G::UNITS) * 16 : kOOB;
       } else {
         row[i] = kRows;
         off[i] = kOOB;
@@ -198,7 +209,7 @@ struct StageDirect {
     for (int j = 0; j < BPW; ++j) {
       const int slot = 64 * (4 * j + w) + lane_id();
       const int r = slot / G::SLOTS_ROW, u = slot % G::SLOTS_ROW;
-      if (r < kRows && u < G::UNITS) {
+      if (r < kRows && u < G::UNITS_D) {
         row[j] = r;
         off[j] = rowoff(r) + u * 16;
       } else {
@@ -231,7 +242,7 @@ struct StageDirect {
 // This lane's fragment (row lane%32, k values 16*kc + 8*(lane/32) .. +8) of
 // an LDS tile.
 template <int DT, int D>
-__device__ __forceinline__ void read_frag(Chunk<DT> (&f)[D / Elem<DT>::KW], const char *tile) {
+__device__ __forceinline__ void read_frag(Chunk<DT> (&f)[kch(DT, D)], const char *tile) {
   using G = Geom<DT, D>;
   const int lane = lane_id();
   const char *p = tile + (lane & 31) * G::RS + (lane >> 5) * (G::KW / 2) * G::ES;
@@ -241,7 +252,7 @@ __device__ __forceinline__ void read_frag(Chunk<DT> (&f)[D / Elem<DT>::KW], cons
 
 // Load the resident fragments of NG 32-row groups straight from global memory.
 template <int DT, int D, int NG, typename RowPtr>
-__device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / Elem<DT>::KW], RowPtr rowptr) {
+__device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][kch(DT, D)], RowPtr rowptr) {
   using G = Geom<DT, D>;
   const int lane = lane_id();
 #pragma unroll
@@ -250,7 +261,7 @@ __device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / Elem<DT>:
 #pragma unroll
     for (int kc = 0; kc < G::KCH; ++kc) {
       const int e = G::KW * kc + (G::KW / 2) * (lane >> 5);
-      if (p != nullptr) load_chunk<DT>(res[n][kc], p + e * G::ES);
+      if (p != nullptr && e < D) load_chunk<DT>(res[n][kc], p + e * G::ES);
       else zero_chunk<DT>(res[n][kc]);
     }
   }
@@ -259,8 +270,8 @@ __device__ __forceinline__ void load_resident(Chunk<DT> (&res)[NG][D / Elem<DT>:
 // acc[n] = A . R[n]^T for one streamed tile against all NG resident groups,
 // k chunks outermost so that the NG accumulation chains are independent.
 template <int DT, int D, int NG>
-__device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[D / Elem<DT>::KW],
-                                         const Chunk<DT> (&res)[NG][D / Elem<DT>::KW],
+__device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[kch(DT, D)],
+                                         const Chunk<DT> (&res)[NG][kch(DT, D)],
                                          f32x16 (&acc)[NG]) {
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
@@ -268,7 +279,7 @@ __device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[D / Elem<DT>::KW]
     for (int v = 0; v < 16; ++v) acc[n][v] = 0.f;
   }
 #pragma unroll
-  for (int kc = 0; kc < D / Elem<DT>::KW; ++kc) {
+  for (int kc = 0; kc < kch(DT, D); ++kc) {
 #pragma unroll
     for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[kc], res[n][kc], acc[n]);
   }

@@ -103,9 +103,9 @@ typedef struct {
 /* One attention layer's queries and keys.  q is [T, Hq, head_dim] and k is
  * [T, Hkv, head_dim] with arbitrary token and head strides (in ELEMENTS) and a
  * contiguous last dimension.  Query head h reads KV head h / (Hq / Hkv).
- * Requirements: Hq % Hkv == 0; head_dim in {64, 80, 96, 128} ({64, 128} for
- * TSEL_FP8_E4M3); q and k 16-byte aligned; both strides multiples of 16
- * bytes.  softmax_scale <= 0 selects
+ * Requirements: Hq % Hkv == 0; head_dim in {64, 72, 80, 96, 128} ({64, 128}
+ * for TSEL_FP8_E4M3; 72 runs as 80 with zero padding); q and k 16-byte
+ * aligned; both strides multiples of 16 bytes.  softmax_scale <= 0 selects
  * 1/sqrt(head_dim) (LiteVLM review, formula section). */
 typedef struct {
   tsel_dtype_t dtype;

@@ -58,7 +58,8 @@ def check(prob, out, lse, ref_o, ref_lse, v=None, rows=None):
 
 SMALL = [("full", "bf16", 4, 4, 64), ("causal", "bf16", 8, 2, 128), ("blockdiag", "bf16", 6, 2, 96),
          ("causal", "f16", 16, 1, 80), ("full", "f16", 3, 3, 96), ("causal", "bf16", 12, 4, 80),
-         ("blockdiag", "f16", 4, 4, 128), ("causal", "f16", 32, 2, 64)]
+         ("blockdiag", "f16", 4, 4, 128), ("causal", "f16", 32, 2, 64), ("blockdiag", "bf16", 4, 4, 72),
+         ("causal", "f16", 8, 2, 72)]
 
 
 @pytest.mark.parametrize("i", range(len(SMALL)))

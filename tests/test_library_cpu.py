@@ -95,7 +95,7 @@ def call_lse(lib, a, lay, out=FAKE):
 
 def test_attn_validation_codes(lib):
     lay = good_layout()
-    assert call_lse(lib, attn(d=72), lay) == B.TSEL_EUNSUPPORTED
+    assert call_lse(lib, attn(d=112), lay) == B.TSEL_EUNSUPPORTED
     assert "head_dim" in last_error(lib)
     assert call_lse(lib, attn(dtype=7), lay) == B.TSEL_EUNSUPPORTED
     assert call_lse(lib, attn(hq=6, hkv=4), lay) == B.TSEL_EINVAL
@@ -113,6 +113,7 @@ def test_attn_validation_codes(lib):
     # fp8 inputs take whole 64-wide k chunks only.
     assert call_lse(lib, attn(dtype=B.TSEL_FP8_E4M3, d=96), lay) == B.TSEL_EUNSUPPORTED
     assert "fp8" in last_error(lib)
+    assert call_lse(lib, attn(dtype=B.TSEL_FP8_E4M3, d=72), lay) == B.TSEL_EUNSUPPORTED
     # A 32-row tile must span less than 2 GiB of the buffers it is read from.
     assert call_lse(lib, attn(st=(1 << 28, 128)), lay) == B.TSEL_EUNSUPPORTED
     assert "2 GiB" in last_error(lib)

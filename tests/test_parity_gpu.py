@@ -43,6 +43,7 @@ SMALL = [(s, m, dt, hq, hkv, d) for s, (m, dt, hq, hkv, d) in enumerate([
     ("full", "bf16", 8, 2, 128), ("causal", "bf16", 4, 1, 80), ("blockdiag", "bf16", 6, 2, 96),
     ("full", "f16", 3, 3, 96), ("causal", "f16", 16, 1, 64), ("blockdiag", "f16", 4, 4, 80),
     ("causal", "bf16", 12, 4, 128), ("full", "bf16", 32, 2, 64), ("causal", "f32", 2, 2, 96),
+    ("full", "bf16", 4, 4, 72), ("blockdiag", "f16", 4, 2, 72), ("causal", "f32", 2, 1, 72),
 ])]
 
 
@@ -55,7 +56,8 @@ def test_small_random(dev, seed, mask, dtype, hq, hkv, d):
 
 
 MEDIUM = [("causal", "bf16", 8, 1, 128), ("full", "f16", 16, 4, 80), ("blockdiag", "bf16", 4, 4, 64),
-          ("causal", "f32", 4, 2, 64), ("causal", "f16", 64, 8, 128), ("full", "bf16", 2, 2, 96)]
+          ("causal", "f32", 4, 2, 64), ("causal", "f16", 64, 8, 128), ("full", "bf16", 2, 2, 96),
+          ("blockdiag", "bf16", 16, 16, 72)]
 
 
 @pytest.mark.parametrize("i", range(len(MEDIUM)))
