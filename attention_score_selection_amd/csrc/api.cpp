@@ -287,10 +287,10 @@ static void job_weights(const tsel_attn_t *a, const tsel_layout_t *l, const Attn
 // head block by head block.  The forward keeps enumeration order: its jobs
 // also stream V, and mixing requests within an XCD costs it more L2 reuse than
 // the order wins (measured on an 8-request varlen batch).
-static void set_order(AttnArgs &x, const tsel_attn_t *a, const tsel_layout_t *l, const AttnPlan &p,
-                      bool keyblocks, int mode) {
+static void set_order(AttnArgs &x, JobPerm &perm, const tsel_attn_t *a, const tsel_layout_t *l,
+                      const AttnPlan &p, bool keyblocks, int mode) {
   x.order = kOrderPlain;
-  memset(x.perm, 0, sizeof(x.perm));
+  memset(perm.w, 0, sizeof(perm.w));
   if (mode == kOrderPlain || p.nseg < 2 || p.jobs_per_hb > kOrderMaxJobs) return;
   std::vector<int> w;
   job_weights(a, l, p, keyblocks, w);
@@ -302,7 +302,7 @@ static void set_order(AttnArgs &x, const tsel_attn_t *a, const tsel_layout_t *l,
   for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int)i;
   std::stable_sort(idx.begin(), idx.end(), [&](int i, int j) { return w[i] > w[j]; });
   for (size_t i = 0; i < idx.size(); ++i)
-    x.perm[i >> 1] |= (unsigned)idx[i] << (16 * (i & 1));
+    perm.w[i >> 1] |= (unsigned)idx[i] << (16 * (i & 1));
   x.order = (mode == kOrderRankMajor && p.nhb % 8 == 0) ? kOrderRankMajor : kOrderSorted;
 }
 
@@ -385,9 +385,10 @@ int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, v
   AttnPlan p;
   if ((rc = plan_lse(attn, layout, &p)) != TSEL_OK) return rc;
   AttnArgs a = attn_args(attn, layout, p);
-  set_order(a, attn, layout, p, false, kOrderSorted);
+  JobPerm perm;
+  set_order(a, perm, attn, layout, p, false, kOrderSorted);
   a.lse_out = lse;
-  const hipError_t e = launch_lse(p, a, (hipStream_t)stream);
+  const hipError_t e = launch_lse(p, a, a.order != kOrderPlain ? &perm : nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_lse launch: %s", hipGetErrorString(e));
   return TSEL_OK;
 }
@@ -409,10 +410,12 @@ int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const fl
                 workspace_bytes);
   if ((uintptr_t)workspace & 15) return fail(TSEL_EINVAL, "workspace must be 16-byte aligned");
   AttnArgs a = attn_args(attn, layout, p);
-  set_order(a, attn, layout, p, true, kOrderRankMajor);
+  JobPerm perm;
+  set_order(a, perm, attn, layout, p, true, kOrderRankMajor);
   a.lse_in = lse;
   a.partial = reinterpret_cast<float *>(workspace);
-  const hipError_t e = launch_colscore(p, a, score, (hipStream_t)stream);
+  const hipError_t e =
+      launch_colscore(p, a, a.order != kOrderPlain ? &perm : nullptr, score, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_colscore launch: %s", hipGetErrorString(e));
   return TSEL_OK;
 }

@@ -110,8 +110,18 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, i
   }
 }
 
-template <int DT, int D, int NG>
-__global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
+// Kernel argument carrying the job permutation (ORD) or nothing.
+template <bool ORD> struct PermArg {};
+template <> struct PermArg<true> { JobPerm p; };
+
+template <bool ORD>
+__device__ __forceinline__ void job_of(const AttnArgs &a, const PermArg<ORD> &pa, int job, int &hb, int &rj) {
+  if constexpr (ORD) job_ordered(a, pa.p, job, hb, rj);
+  else job_plain(a, job, hb, rj);
+}
+
+template <int DT, int D, int NG, bool ORD>
+__global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa) {
   using G = Geom<DT, D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::TILE];
   __shared__ int s_bad;
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
     return (hi - lo + TB - 1) / TB;
   };
   int hb, rj;
-  job_order(a, job, hb, rj);
+  job_of<ORD>(a, pa, job, hb, rj);
   int local;
   const int seg = find_segment(a.nseg, rj, count, local);
   if (seg < 0) return;
@@ -213,8 +223,8 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a) {
 // heads) and their LSE stream through LDS; per-column partial sums go to
 // partial[(hb*RCmax + rc)*N + c].
 // ---------------------------------------------------------------------------
-template <int DT, int D, int NG>
-__global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
+template <int DT, int D, int NG, bool ORD>
+__global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
   using G = Geom<DT, D>;
   constexpr int BUF = G::TILE + kRows * 4;  // tile + 32 floats of LSE (log2 units)
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a) {
     return ((ch - cl + KB - 1) / KB) * ((hi - lo + RC - 1) / RC);
   };
   int hb, rj;
-  job_order(a, job, hb, rj);
+  job_of<ORD>(a, pa, job, hb, rj);
   int local;
   const int seg = find_segment(a.nseg, rj, count, local);
   if (seg < 0) return;
@@ -443,83 +453,103 @@ namespace {
 template <int DT, int D>
 constexpr int kNGMax = max_groups(DT, D);
 
+// The permuted variants exist for the widest group count only (the
+// one-group fallback serves small grids, where order matters little).
 template <int DT, int D, int NG>
-hipError_t lse_go(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+hipError_t lse_go(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   const int grid = (int)((p.total_jobs + 7) / 8 * 8);
-  hipLaunchKernelGGL((lse_kernel<DT, D, NG>), dim3(grid), dim3(256), 0, s, a);
+  if constexpr (NG == kNGMax<DT, D>) {
+    if (perm != nullptr) {
+      hipLaunchKernelGGL((lse_kernel<DT, D, NG, true>), dim3(grid), dim3(256), 0, s, a, PermArg<true>{*perm});
+      return hipGetLastError();
+    }
+  }
+  AttnArgs b = a;
+  b.order = kOrderPlain;
+  hipLaunchKernelGGL((lse_kernel<DT, D, NG, false>), dim3(grid), dim3(256), 0, s, b, PermArg<false>{});
   return hipGetLastError();
 }
 
 template <int DT, int D, int NG>
-hipError_t col_go(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+hipError_t col_go(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   const int grid = (int)((p.total_jobs + 7) / 8 * 8);
-  hipLaunchKernelGGL((colscore_kernel<DT, D, NG>), dim3(grid), dim3(256), 0, s, a);
+  if constexpr (NG == kNGMax<DT, D>) {
+    if (perm != nullptr) {
+      hipLaunchKernelGGL((colscore_kernel<DT, D, NG, true>), dim3(grid), dim3(256), 0, s, a,
+                         PermArg<true>{*perm});
+      return hipGetLastError();
+    }
+  }
+  AttnArgs b = a;
+  b.order = kOrderPlain;
+  hipLaunchKernelGGL((colscore_kernel<DT, D, NG, false>), dim3(grid), dim3(256), 0, s, b, PermArg<false>{});
   return hipGetLastError();
 }
 
 template <int DT, int D>
-hipError_t lse_ng(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
-  if (p.NT == kNGMax<DT, D>) return lse_go<DT, D, kNGMax<DT, D>>(p, a, s);
-  return lse_go<DT, D, 1>(p, a, s);
+hipError_t lse_ng(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
+  if (p.NT == kNGMax<DT, D>) return lse_go<DT, D, kNGMax<DT, D>>(p, a, perm, s);
+  return lse_go<DT, D, 1>(p, a, perm, s);
 }
 template <int DT, int D>
-hipError_t col_ng(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
-  if (p.NT == kNGMax<DT, D>) return col_go<DT, D, kNGMax<DT, D>>(p, a, s);
-  return col_go<DT, D, 1>(p, a, s);
+hipError_t col_ng(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
+  if (p.NT == kNGMax<DT, D>) return col_go<DT, D, kNGMax<DT, D>>(p, a, perm, s);
+  return col_go<DT, D, 1>(p, a, perm, s);
 }
 
 // fp8 runs head_dim 64 and 128 only (whole 64-wide k chunks); the host
 // rejects the others before any launch.
 template <int DT>
-hipError_t lse_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+hipError_t lse_d(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   if constexpr (DT == TSEL_FP8_E4M3) {
-    return p.D == 64 ? lse_ng<DT, 64>(p, a, s) : lse_ng<DT, 128>(p, a, s);
+    return p.D == 64 ? lse_ng<DT, 64>(p, a, perm, s) : lse_ng<DT, 128>(p, a, perm, s);
   } else {
     switch (p.D) {
-      case 64: return lse_ng<DT, 64>(p, a, s);
-      case 72: return lse_ng<DT, 72>(p, a, s);
-      case 80: return lse_ng<DT, 80>(p, a, s);
-      case 96: return lse_ng<DT, 96>(p, a, s);
-      default: return lse_ng<DT, 128>(p, a, s);
+      case 64: return lse_ng<DT, 64>(p, a, perm, s);
+      case 72: return lse_ng<DT, 72>(p, a, perm, s);
+      case 80: return lse_ng<DT, 80>(p, a, perm, s);
+      case 96: return lse_ng<DT, 96>(p, a, perm, s);
+      default: return lse_ng<DT, 128>(p, a, perm, s);
     }
   }
 }
 template <int DT>
-hipError_t col_d(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+hipError_t col_d(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   if constexpr (DT == TSEL_FP8_E4M3) {
-    return p.D == 64 ? col_ng<DT, 64>(p, a, s) : col_ng<DT, 128>(p, a, s);
+    return p.D == 64 ? col_ng<DT, 64>(p, a, perm, s) : col_ng<DT, 128>(p, a, perm, s);
   } else {
     switch (p.D) {
-      case 64: return col_ng<DT, 64>(p, a, s);
-      case 72: return col_ng<DT, 72>(p, a, s);
-      case 80: return col_ng<DT, 80>(p, a, s);
-      case 96: return col_ng<DT, 96>(p, a, s);
-      default: return col_ng<DT, 128>(p, a, s);
+      case 64: return col_ng<DT, 64>(p, a, perm, s);
+      case 72: return col_ng<DT, 72>(p, a, perm, s);
+      case 80: return col_ng<DT, 80>(p, a, perm, s);
+      case 96: return col_ng<DT, 96>(p, a, perm, s);
+      default: return col_ng<DT, 128>(p, a, perm, s);
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, hipStream_t s) {
+hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   if (p.total_jobs == 0) return hipSuccess;
   switch (p.dtype) {
-    case TSEL_F32: return lse_d<TSEL_F32>(p, a, s);
-    case TSEL_F16: return lse_d<TSEL_F16>(p, a, s);
-    case TSEL_FP8_E4M3: return lse_d<TSEL_FP8_E4M3>(p, a, s);
-    default: return lse_d<TSEL_BF16>(p, a, s);
+    case TSEL_F32: return lse_d<TSEL_F32>(p, a, perm, s);
+    case TSEL_F16: return lse_d<TSEL_F16>(p, a, perm, s);
+    case TSEL_FP8_E4M3: return lse_d<TSEL_FP8_E4M3>(p, a, perm, s);
+    default: return lse_d<TSEL_BF16>(p, a, perm, s);
   }
 }
 
-hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, float *score, hipStream_t s) {
+hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, float *score,
+                           hipStream_t s) {
   if (a.N == 0) return hipSuccess;
   hipError_t e = hipSuccess;
   if (p.total_jobs > 0) {
     switch (p.dtype) {
-      case TSEL_F32: e = col_d<TSEL_F32>(p, a, s); break;
-      case TSEL_F16: e = col_d<TSEL_F16>(p, a, s); break;
-      case TSEL_FP8_E4M3: e = col_d<TSEL_FP8_E4M3>(p, a, s); break;
-      default: e = col_d<TSEL_BF16>(p, a, s); break;
+      case TSEL_F32: e = col_d<TSEL_F32>(p, a, perm, s); break;
+      case TSEL_F16: e = col_d<TSEL_F16>(p, a, perm, s); break;
+      case TSEL_FP8_E4M3: e = col_d<TSEL_FP8_E4M3>(p, a, perm, s); break;
+      default: e = col_d<TSEL_BF16>(p, a, perm, s); break;
     }
     if (e != hipSuccess) return e;
   }

@@ -110,12 +110,19 @@ __device__ __forceinline__ int find_segment(int nseg, int idx, CountFn count, in
 }
 
 // A workgroup's head block hb and job rj (within the head block) from its
-// job index.  kOrderPlain: enumeration order (segment by segment), head block
-// by head block.  Otherwise rj comes from the host's heaviest-first
-// permutation: kOrderRankMajor runs an XCD's jobs rank by rank across the head
-// blocks it holds (the head blocks are a multiple of 8, a contiguous group of
-// them per XCD, see xcd_job); kOrderSorted keeps head block by head block.
-__device__ __forceinline__ void job_order(const AttnArgs &a, int job, int &hb, int &rj) {
+// job index, in enumeration order (segment by segment), head block by head
+// block.
+__device__ __forceinline__ void job_plain(const AttnArgs &a, int job, int &hb, int &rj) {
+  hb = job / a.jobs_per_hb;
+  rj = job % a.jobs_per_hb;
+}
+
+// The same from the host's heaviest-first permutation: kOrderRankMajor runs an
+// XCD's jobs rank by rank across the head blocks it holds (the head blocks
+// are a multiple of 8, a contiguous group of them per XCD, see xcd_job);
+// kOrderSorted keeps head block by head block.
+__device__ __forceinline__ void job_ordered(const AttnArgs &a, const JobPerm &perm, int job, int &hb,
+                                            int &rj) {
   int r;
   if (a.order == kOrderRankMajor) {
     const int H = a.nhb >> 3, per = H * a.jobs_per_hb;
@@ -126,12 +133,8 @@ __device__ __forceinline__ void job_order(const AttnArgs &a, int job, int &hb, i
     hb = job / a.jobs_per_hb;
     r = job % a.jobs_per_hb;
   }
-  if (a.order == kOrderPlain) {
-    rj = r;
-  } else {
-    const unsigned w = uni((int)a.perm[r >> 1]);  // two 16-bit entries per word (scalar load)
-    rj = (int)((r & 1) ? (w >> 16) : (w & 0xffffu));
-  }
+  const unsigned w = uni((int)perm.w[r >> 1]);  // two 16-bit entries per word (scalar load)
+  rj = (int)((r & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
 }  // namespace tsel

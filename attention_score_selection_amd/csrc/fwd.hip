@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs fa) {
     return (hi - lo + TB - 1) / TB;
   };
   int hb, rj;
-  job_order(a, job, hb, rj);
+  job_plain(a, job, hb, rj);
   int local;
   const int seg = find_segment(a.nseg, rj, count, local);
   if (seg < 0) return;

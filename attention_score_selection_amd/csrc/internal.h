@@ -23,9 +23,14 @@ enum SegKind { SEG_REQ = 0, SEG_IMG = 1 };
 
 // Order in which a launch runs the jobs of a head block (see job_order).  A
 // permutation travels in the kernel arguments, so launches with at most
-// kOrderMaxJobs jobs per head block can be reordered.
+// kOrderMaxJobs jobs per head block can be reordered.  Only the reordered
+// launches carry it: a kilobyte more of kernel arguments measured 6% slower
+// on the column score.
 enum JobOrder { kOrderPlain = 0, kOrderRankMajor = 1, kOrderSorted = 2 };
 constexpr int kOrderMaxJobs = 512;
+struct JobPerm {
+  unsigned w[kOrderMaxJobs / 2];  // heaviest-first job permutation, 16 bits per entry (low half first)
+};
 
 // Parameters of the LSE and column-score kernels.
 struct AttnArgs {
@@ -44,7 +49,6 @@ struct AttnArgs {
   int jobs_per_hb;       // jobs of one head block
   int total_jobs;        // nhb * jobs_per_hb
   int order;             // JobOrder
-  unsigned perm[kOrderMaxJobs / 2];   // heaviest-first job permutation, 16 bits per entry (low half first)
   // LSE kernel
   float *lse_out;
   int TB;                // tokens per row block
@@ -80,8 +84,10 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
 int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
 
 // Kernel launchers (attn.hip / select.hip).  Return hipError_t of the launch.
-hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, hipStream_t s);
-hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, float *score, hipStream_t s);
+// perm: the job permutation when a.order is not kOrderPlain, else null.
+hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s);
+hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, float *score,
+                           hipStream_t s);
 hipError_t launch_fwd(const AttnPlan &p, const FwdArgs &a, hipStream_t s);
 int plan_fwd(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p);
 
