@@ -206,6 +206,34 @@ def test_large_shapes_value_sensitive(dev, cfg):
     P.full_check(prob, got, ref, prob.emb)
 
 
+def test_long_sequence_properties(dev):
+    """One 98304-token request (96 images of 32x32, so every token is a
+    candidate), causal, 2/1 heads, d = 64: many row chunks and key blocks per
+    head block.  Checks the LSE of sampled rows against the row-at-a-time
+    oracle and, at full size, the identity sum_c mass_c = Hq * T (each row's
+    probabilities sum to one and every key is a candidate) to 1e-4, plus the
+    kept count and compacted length."""
+    T = 98304
+    imgs = [(i * 1024, 32, 32) for i in range(96)]
+    prob = make_problem("long_98304_h2_d64_causal", [(T, imgs)], 2, 1, 64, "bf16", "causal", 1.0, 106,
+                        ratios=0.5, emb_dim=16)
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    q, k = prob.q.to(dev), prob.k.to(dev)
+    out = tsel.select(q, k, lay, "causal", prob.keep_ratio)
+    torch.cuda.synchronize(dev)
+    mass_total = float(out["score"].double().sum()) * prob.hq * T
+    print(f"[check] sum of column masses {mass_total:.6f} vs Hq*T = {prob.hq * T}", flush=True)
+    assert abs(mass_total - prob.hq * T) <= 1e-4 * prob.hq * T
+    rows = np.linspace(0, T - 1, 16).astype(int)
+    ref = oracle.lse_rows(prob, rows)
+    got = out["lse"].cpu().double().numpy()[:, rows]
+    assert np.max(np.abs(got - ref)) <= 1e-4
+    kept = int(out["keep"].sum())
+    assert kept == int(out["k"][0]) == oracle.budget_k(0.5, T)
+    assert int(out["compact"]["cu_seqlens"][-1]) == kept
+
+
 # ---------------------------------------------------------------------------
 # Edge cases.
 # ---------------------------------------------------------------------------
