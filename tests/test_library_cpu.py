@@ -8,6 +8,8 @@ validation, so no kernel is launched.
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -223,3 +225,28 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+# ---------------------------------------------------------------------------
+# The C ABI from C: the header alone compiles as strict C99 and as C++11, and
+# a plain-C program (tests/c_consumer) links the library and sees its
+# validation contract.  No GPU is touched.
+# ---------------------------------------------------------------------------
+
+def test_header_is_plain_c_and_cpp(tmp_path):
+    src = tmp_path / "hdr.c"
+    src.write_text('#include "tsel.h"\nint main(void) { return tsel_version() == TSEL_VERSION ? 0 : 1; }\n')
+    inc = os.path.dirname(HEADER)
+    for cmd in (["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only"],
+                ["g++", "-std=c++11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", "c++"]):
+        r = subprocess.run(cmd + ["-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_c_consumer_host_checks(lib):
+    sys.path.insert(0, os.path.join(os.path.dirname(__file__), "c_consumer"))
+    import build_consumer
+    exe = build_consumer.BIN if os.path.exists(build_consumer.BIN) else build_consumer.build()
+    r = subprocess.run([exe, "check"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "check ok" in r.stdout
