@@ -174,8 +174,9 @@ int plan_fwd(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
 }
 
 // Key blocks of 4 waves x NG resident 32-key groups; row chunks of ~8192
-// streamed rows, halved while the grid is small.  One partial per
-// (head block, row chunk, candidate).
+// streamed rows, halved while the grid has fewer jobs than two workgroups
+// per CU (halving further measured slower: more per-job setup).  One
+// partial per (head block, row chunk, candidate).
 int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
   if (int rc = check_offsets(a, l, p->F)) return rc;
@@ -200,7 +201,7 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
       p->RC = (int)rc;
       p->jobs_per_hb = J;
       p->total_jobs = J * p->nhb;
-      if (p->total_jobs >= 1024 || rc < 64) break;
+      if (p->total_jobs >= 512 || rc < 64) break;
       rc = (rc / 2 + 31) / 32 * 32;
     }
     if (p->total_jobs >= 512 || ng == 1) break;
