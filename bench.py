@@ -158,6 +158,8 @@ def main():
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
     ap.add_argument("--forward", action="store_true",
                     help="also time the attention forward (tsel_attention_fwd) on the same layer")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--mass-tau", type=float, default=None,
                     help="also time the input-dependent budget (tsel_budget_mass) at this mass fraction")
     ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=4,
@@ -280,6 +282,25 @@ def main():
     }
     if args.forward:
         result["attention_forward"] = time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems)
+    if args.graph:
+        # The same step captured once in a HIP graph and replayed (the library
+        # only enqueues kernels, so the whole step is capturable).
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        gev[0].record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        gev[1].record(stream)
+        torch.cuda.synchronize(dev)
+        result["graph_replay"] = {"ms_per_step": gev[0].elapsed_time(gev[1]) / args.steps}
     if args.mass_tau is not None:
         result["budget_mass"] = time_mass(tsel, prob, score, lay, dev, stream, args)
     if args.calib_copy_mb > 0:
