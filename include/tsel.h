@@ -40,7 +40,9 @@
  *   tsel_last_error() (thread-local) describes the problem.  On success it
  *   returns TSEL_OK after enqueuing its kernels on `stream` (a hipStream_t;
  *   NULL is the null stream).  No call synchronises the device or copies
- *   device memory to the host.
+ *   device memory to the host; calls enqueue kernel launches only (no
+ *   allocation, copy or memset), so a caller may capture them in a HIP graph
+ *   and replay it while the layout, sizes and buffers stay the same.
  * - Device array contents are trusted to equal their host mirrors.
  * - Results are deterministic: no floating-point atomics; every reduction
  *   runs in a fixed order.
