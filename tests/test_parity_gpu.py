@@ -238,6 +238,35 @@ def test_long_sequence_properties(dev):
 # Edge cases.
 # ---------------------------------------------------------------------------
 
+def test_many_requests_multi_launch_budgets(dev):
+    """300 requests (more than one 256-pool top-k launch and several 64-pool
+    mass-budget launches), each a short text run around one small image, and
+    a few imageless requests: the whole path against the oracle, plus the
+    mass budget on the GPU scores."""
+    rng = np.random.default_rng(110)
+    reqs = []
+    for b in range(300):
+        if b % 37 == 5:
+            reqs.append((int(rng.integers(1, 9)), []))
+            continue
+        h, w = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        pre = int(rng.integers(0, 4))
+        reqs.append((pre + h * w + int(rng.integers(0, 4)), [(pre, h, w)]))
+    prob = make_problem("many_300req_h4x2_d64", reqs, 4, 2, 64, "bf16", "causal", 1.0, 111,
+                        ratio_range=(0.2, 0.9), emb_dim=16)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+    lay = tsel.Layout.from_problem(prob, dev)
+    score = got["score"].astype(np.float32)
+    tau = list(rng.random(prob.B))
+    keep, k = tsel.tsel_budget_mass(lay, torch.from_numpy(score).to(dev), tau, [0.1] * prob.B, [0.9] * prob.B)
+    torch.cuda.synchronize(dev)
+    ref_keep, ref_k = oracle.mass_budget(prob, score.astype(np.float64), tau, [0.1] * prob.B, [0.9] * prob.B)
+    assert np.array_equal(k.cpu().numpy(), ref_k)
+    assert np.array_equal(keep.cpu().numpy(), ref_keep)
+
+
 def test_keep_nothing_and_everything(dev):
     prob = random_small(31, "causal", dtype="bf16", hq=4, hkv=2, d=64, n_req=3)
     prob.keep_ratio = np.array([0.0, 1.0, 0.5])
