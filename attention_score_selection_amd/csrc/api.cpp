@@ -2,10 +2,12 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -26,6 +28,37 @@ int fail(int code, const char *fmt, ...) {
 void clear_error() { g_err.clear(); }
 
 static int elem_size(int dt) { return dt == TSEL_F32 ? 4 : dt == TSEL_FP8_E4M3 ? 1 : 2; }
+
+// With TSEL_DEBUG=1 in the environment, every call also checks that the
+// device layout arrays equal their host mirrors, through a synchronous
+// device-to-host copy (debugging only: otherwise the device arrays are
+// trusted and no call reads device memory back).
+static int check_device_mirrors(const tsel_layout_t *l) {
+  const char *dbg = getenv("TSEL_DEBUG");
+  if (dbg == nullptr || dbg[0] != '1') return TSEL_OK;
+  const size_t B = (size_t)l->num_reqs, S = (size_t)l->num_images;
+  const struct {
+    const int32_t *d, *h;
+    size_t n;
+    const char *name;
+  } arr[] = {{l->cu_seqlens, l->cu_seqlens_h, B + 1, "cu_seqlens"},
+             {l->cu_images, l->cu_images_h, B + 1, "cu_images"},
+             {l->img_start, l->img_start_h, S, "img_start"},
+             {l->img_hw, l->img_hw_h, 2 * S, "img_hw"},
+             {l->cu_cands, l->cu_cands_h, S + 1, "cu_cands"}};
+  std::vector<int32_t> tmp;
+  for (const auto &x : arr) {
+    if (x.n == 0) continue;
+    tmp.resize(x.n);
+    const hipError_t e = hipMemcpy(tmp.data(), x.d, x.n * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(TSEL_EHIP, "TSEL_DEBUG: reading device %s: %s", x.name, hipGetErrorString(e));
+    for (size_t i = 0; i < x.n; ++i)
+      if (tmp[i] != x.h[i])
+        return fail(TSEL_EINVAL, "TSEL_DEBUG: device %s[%zu] = %d differs from its host mirror (%d)", x.name, i,
+                    tmp[i], x.h[i]);
+  }
+  return TSEL_OK;
+}
 
 static int check_layout(const tsel_layout_t *l) {
   if (l == nullptr) return fail(TSEL_EINVAL, "layout is NULL");
@@ -57,7 +90,7 @@ static int check_layout(const tsel_layout_t *l) {
       prev_end = (int)end;
     }
   }
-  return TSEL_OK;
+  return check_device_mirrors(l);
 }
 
 static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {

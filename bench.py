@@ -96,7 +96,14 @@ def cpu_baseline(prob, elems_per_head, budget_s=10.0):
         dt += time.perf_counter() - t0
         done += 1
     elems = elems_per_head * done * hg
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": elems / dt, "unit": "score elements/s", "cores": workers, "kind": "oracle",
+            "cpu_model": model,
             "sample": f"fp64 LSE + column mass of query heads 0-{done * hg - 1} "
                       f"({done} KV group(s), {elems:.4g} elements) of the same workload, {dt:.1f} s"}
 
@@ -158,6 +165,8 @@ def main():
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
     ap.add_argument("--forward", action="store_true",
                     help="also time the attention forward (tsel_attention_fwd) on the same layer")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single steps after evicting the caches (median of 3)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--mass-tau", type=float, default=None,
@@ -265,6 +274,7 @@ def main():
                    "head_dim": d, "mask": prob.mask, "vision_candidates": prob.N, "images": prob.S,
                    "keep_ratio": float(ratios[0]) if len(ratios) == 1 else [float(r) for r in ratios],
                    "kept_vision": kept, "tokens_out": t_out,
+                   "dense_score_elements": prob.hq * prob.T * prob.N,
                    "emb_dim": prob.emb_dim,
                    "lse": "supplied (not timed)" if prob.lse_supplied else "computed in-library"},
         "phases_ms": {"lse": t_lse * 1e3, "colscore": t_col * 1e3, "budget_topk": t_topk * 1e3,
@@ -282,6 +292,22 @@ def main():
     }
     if args.forward:
         result["attention_forward"] = time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems)
+    if args.cold:
+        # One step after evicting the caches (writing a buffer four times the
+        # 256 MB MALL), three times; the median is reported.
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(3):
+            flush.fill_(1)
+            torch.cuda.synchronize(dev)
+            ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ce[0].record(stream)
+            step()
+            ce[1].record(stream)
+            torch.cuda.synchronize(dev)
+            cold.append(ce[0].elapsed_time(ce[1]))
+        del flush
+        result["cold_step_ms"] = float(np.median(cold))
     if args.graph:
         # The same step captured once in a HIP graph and replayed (the library
         # only enqueues kernels, so the whole step is capturable).

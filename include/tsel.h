@@ -43,7 +43,10 @@
  *   device memory to the host; calls enqueue kernel launches only (no
  *   allocation, copy or memset), so a caller may capture them in a HIP graph
  *   and replay it while the layout, sizes and buffers stay the same.
- * - Device array contents are trusted to equal their host mirrors.
+ * - Device array contents are trusted to equal their host mirrors; with
+ *   TSEL_DEBUG=1 in the environment every call first checks that they do
+ *   (a synchronous device-to-host copy, for debugging) and returns
+ *   TSEL_EINVAL when they differ.
  * - Results are deterministic: no floating-point atomics; every reduction
  *   runs in a fixed order.
  */

@@ -267,6 +267,31 @@ def test_many_requests_multi_launch_budgets(dev):
     assert np.array_equal(keep.cpu().numpy(), ref_keep)
 
 
+def test_debug_mode_checks_device_mirrors(dev, monkeypatch):
+    """TSEL_DEBUG=1: a call first compares the device layout arrays with their
+    host mirrors.  Consistent arrays pass and give the usual result; a device
+    array that differs is rejected before any kernel runs (the layout is never
+    used without the check while it is inconsistent)."""
+    prob = random_small(61, "causal", dtype="bf16", hq=4, hkv=2, d=64, n_req=3)
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    q, k = prob.q.to(dev), prob.k.to(dev)
+    ref = tsel.tsel_lse(q, k, lay, "causal")
+    monkeypatch.setenv("TSEL_DEBUG", "1")
+    got = tsel.tsel_lse(q, k, lay, "causal")
+    torch.cuda.synchronize(dev)
+    assert torch.equal(got, ref)
+    lay.d["cu_cands"][1] += 1
+    torch.cuda.synchronize(dev)
+    with pytest.raises(tsel.TselError, match="TSEL_DEBUG: device cu_cands"):
+        tsel.tsel_lse(q, k, lay, "causal")
+    with pytest.raises(tsel.TselError, match="TSEL_DEBUG"):
+        tsel.tsel_colscore(q, k, lay, "causal", ref)
+    lay.d["cu_cands"][1] -= 1
+    torch.cuda.synchronize(dev)
+    assert torch.equal(tsel.tsel_lse(q, k, lay, "causal"), ref)
+
+
 def test_keep_nothing_and_everything(dev):
     prob = random_small(31, "causal", dtype="bf16", hq=4, hkv=2, d=64, n_req=3)
     prob.keep_ratio = np.array([0.0, 1.0, 0.5])
