@@ -248,6 +248,7 @@ def main():
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     phase = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in events]) / 1e3
+    step_median_ms = float(np.median([e[0].elapsed_time(e[5]) for e in events]))
     t_lse, t_col, t_topk, t_cmp, t_rope = phase.mean(axis=0)
     ms_per_step = wall / args.steps * 1e3
 
@@ -265,6 +266,7 @@ def main():
         "unit": "score elements/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "step_ms_median": step_median_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": prob.dtype,
         "data": f"synthetic (seeded normal Q/K, std {prob.std:.4g}" +
