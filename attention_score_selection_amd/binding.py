@@ -296,13 +296,20 @@ def tsel_mrope_positions(layout: Layout, compact: dict, out: Optional[torch.Tens
 
 def select(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask: str, keep_ratio,
            emb: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-           softmax_scale: float = 0.0) -> dict:
-    """The whole path: LSE (unless supplied) -> scores -> budget top-k -> compaction
-    -> rotary positions of the compacted sequence."""
+           softmax_scale: float = 0.0, mass=None) -> dict:
+    """The whole path: LSE (unless supplied) -> scores -> budget -> compaction
+    -> rotary positions of the compacted sequence.  The budget is the fixed
+    ratio top-k (keep_ratio), or with ``mass=(tau, r_min, r_max)`` (per-pool
+    sequences) the input-dependent one; its k per pool is then copied to the
+    host to size the compaction (one synchronisation)."""
     if lse is None:
         lse = tsel_lse(q, k, layout, mask, softmax_scale)
     score = tsel_colscore(q, k, layout, mask, lse, softmax_scale)
-    keep, ks = tsel_budget_topk(layout, score, keep_ratio)
+    if mass is None:
+        keep, ks = tsel_budget_topk(layout, score, keep_ratio)
+    else:
+        keep, kd = tsel_budget_mass(layout, score, *mass)
+        ks = kd.cpu().numpy()
     comp = tsel_compact(layout, keep, ks, emb)
     comp["positions"] = tsel_mrope_positions(layout, comp)
     return dict(lse=lse, score=score, keep=keep, k=ks, compact=comp)

@@ -129,3 +129,24 @@ def test_budget_mass_varlen_batch_per_request(dev):
     w = rng.gamma(0.5, size=prob.N)
     score = (w / w.sum()).astype(np.float32)
     run_both(prob, score, list(rng.random(prob.B)), [0.05] * prob.B, [0.95] * prob.B, dev)
+
+
+def test_select_with_mass_budget(dev):
+    """select(..., mass=...) runs the input-dependent budget inside the whole
+    path; the kept set and compaction match the oracle's mass budget on the
+    same GPU scores."""
+    prob = random_medium(47, "causal", dtype="bf16", hq=8, hkv=2, d=128, n_req=3)
+    announce(prob.name)
+    lay = tsel.Layout.from_problem(prob, dev)
+    q, k, emb = prob.q.to(dev), prob.k.to(dev), prob.emb.to(dev)
+    tau, lo, hi = [0.7, 0.9, 0.5], [0.1, 0.2, 0.0], [0.9, 0.95, 1.0]
+    out = tsel.select(q, k, lay, "causal", None, emb=emb, mass=(tau, lo, hi))
+    torch.cuda.synchronize(dev)
+    score = out["score"].cpu().numpy()
+    ref_keep, ref_k = oracle.mass_budget(prob, score.astype(np.float64), tau, lo, hi)
+    assert np.array_equal(np.asarray(out["k"]), ref_k)
+    assert np.array_equal(out["keep"].cpu().numpy(), ref_keep)
+    comp = oracle.compact(prob, ref_keep)
+    assert np.array_equal(out["compact"]["token_idx"].cpu().numpy(), comp["token_idx"])
+    assert np.array_equal(out["compact"]["positions"].cpu().numpy(), comp["positions"])
+    assert torch.equal(out["compact"]["emb"].cpu(), prob.emb[torch.from_numpy(comp["token_idx"])])
