@@ -180,7 +180,7 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     p->total_jobs = R * p->nhb;
     if (p->total_jobs >= 512 || ng == 1) break;
   }
-  p->KB = p->RC = p->RCmax = 0;
+  p->KB = p->RC = p->RCF = p->RCmax = 0;
   p->partial_bytes = 0;
   if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
   return TSEL_OK;
@@ -200,7 +200,7 @@ int plan_fwd(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   }
   p->jobs_per_hb = R;
   p->total_jobs = R * p->nhb;
-  p->KB = p->RC = p->RCmax = 0;
+  p->KB = p->RC = p->RCF = p->RCmax = 0;
   p->partial_bytes = 0;
   if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
   return TSEL_OK;
@@ -220,27 +220,46 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     maxn = std::max(maxn, n);
   }
   const int ng_max = max_groups(a->dtype, a->head_dim);
+  auto plan_jobs = [&](int rc, int rcf) {
+    long long J = 0;
+    for (int s = 0; s < p->nseg; ++s) {
+      long long n, nc;
+      seg_sizes(l, p->segkind, s, n, nc);
+      J += ((nc + p->KB - 1) / p->KB) * chunk_count((int)n, rc, rcf);
+    }
+    p->RC = rc;
+    p->RCF = rcf;
+    p->jobs_per_hb = J;
+    p->total_jobs = J * p->nhb;
+  };
+  // Row chunks of 8192 query rows (RC tokens x F heads); halved while the
+  // grid has fewer than 512 jobs (two workgroups per CU).
+  const int rc_full = std::max(32, 8192 / p->F);
   for (int ng = ng_max;; ng = 1) {
     p->NT = ng;
     p->KB = 4 * ng * 32;
-    long long rc = std::max<long long>(32, 8192 / p->F);
+    int rc = rc_full;
     for (;;) {
-      long long J = 0;
-      for (int s = 0; s < p->nseg; ++s) {
-        long long n, nc;
-        seg_sizes(l, p->segkind, s, n, nc);
-        J += ((nc + p->KB - 1) / p->KB) * ((n + rc - 1) / rc);
-      }
-      p->RC = (int)rc;
-      p->jobs_per_hb = J;
-      p->total_jobs = J * p->nhb;
+      plan_jobs(rc, rc);
       if (p->total_jobs >= 512 || rc < 64) break;
       rc = (rc / 2 + 31) / 32 * 32;
     }
     if (p->total_jobs >= 512 || ng == 1) break;
   }
+  // Full-size chunks and a segment longer than one: the launch runs several
+  // rounds of long jobs, and the last round decides its length.  Cutting each
+  // segment's last chunk in four makes that round short jobs.  On the
+  // 16384-token GQA layer this measured 3% faster with fp8 inputs and 0.5%
+  // with bf16, where the clock rises as the tail leaves CUs idle (pieces of
+  // 2 and 8 measured between).
+  if (p->RC == rc_full && maxn > rc_full) plan_jobs(rc_full, rc_full / 4);
   p->TB = 0;
-  p->RCmax = (int)std::max<long long>(1, (maxn + p->RC - 1) / p->RC);
+  p->RCmax = 1;
+  for (int s = 0; s < p->nseg; ++s) {
+    long long n, nc;
+    seg_sizes(l, p->segkind, s, n, nc);
+    p->RCmax = std::max(p->RCmax, chunk_count((int)n, p->RC, p->RCF));
+  }
   const long long N = l->cu_cands_h[l->num_images];
   p->partial_bytes = (size_t)p->nhb * p->RCmax * N * sizeof(float);
   if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
@@ -294,11 +313,14 @@ static void job_weights(const tsel_attn_t *a, const tsel_layout_t *l, const Attn
       continue;
     }
     const long long cl = l->cu_cands_h[sl], ch = l->cu_cands_h[sh];
-    const long long nkb = (ch - cl + p.KB - 1) / p.KB, nrc = (hi - lo + p.RC - 1) / p.RC;
+    const long long nkb = (ch - cl + p.KB - 1) / p.KB;
+    const int nrc = chunk_count((int)(hi - lo), p.RC, p.RCF);
     const long long tpt = 32 / p.F;
-    for (long long rc = 0; rc < nrc; ++rc)
+    for (int rc = 0; rc < nrc; ++rc)
       for (long long kb = 0; kb < nkb; ++kb) {
-        const long long c_lo = lo + rc * p.RC, c_hi = std::min(c_lo + p.RC, hi);
+        int r0, r1;
+        chunk_range(rc, (int)(hi - lo), p.RC, p.RCF, r0, r1);
+        const long long c_lo = lo + r0, c_hi = lo + r1;
         long long r_lo = c_lo;
         if (causal) {
           const long long c = cl + kb * p.KB;
@@ -364,6 +386,7 @@ static AttnArgs attn_args(const tsel_attn_t *a, const tsel_layout_t *l, const At
   x.TB = p.TB;
   x.N = l->cu_cands_h[l->num_images];
   x.RC = p.RC;
+  x.RCF = p.RCF;
   x.RCmax = p.RCmax;
   x.KB = p.KB;
   return x;

@@ -231,12 +231,12 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<OR
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
-  const int KB = a.KB, RC = a.RC;
+  const int KB = a.KB;
   auto count = [&](int s) {
     int lo, hi, sl, sh, cl, ch;
     seg_tokens(a.L, a.segkind, s, lo, hi);
     seg_images(a.L, a.segkind, s, sl, sh, cl, ch);
-    return ((ch - cl + KB - 1) / KB) * ((hi - lo + RC - 1) / RC);
+    return ((ch - cl + KB - 1) / KB) * chunk_count(hi - lo, a.RC, a.RCF);
   };
   int hb, rj;
   job_of<ORD>(a, pa, job, hb, rj);
@@ -258,8 +258,10 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<OR
   const int rc = local / nkb, kb = local % nkb;
   const int kb0 = c_lo + kb * KB;
   const int kb1 = min(kb0 + KB, c_hi);
-  const int chunk_lo = seg_lo + rc * RC;
-  const int chunk_hi = min(chunk_lo + RC, seg_hi);
+  int chunk_lo, chunk_hi;
+  chunk_range(rc, seg_hi - seg_lo, a.RC, a.RCF, chunk_lo, chunk_hi);
+  chunk_lo = uni(seg_lo + chunk_lo);
+  chunk_hi = uni(seg_lo + chunk_hi);
   const int first_ktok = uni(cand_token(a.L, s_lo, s_hi, kb0));
   const int row_lo = uni(a.causal ? max(chunk_lo, first_ktok) : chunk_lo);
   if (row_lo >= chunk_hi) return;  // no row of this chunk sees any key of the block
@@ -420,8 +422,8 @@ __global__ __launch_bounds__(256) void colscore_finalize(AttnArgs a, float *scor
     int seg_lo, seg_hi;
     seg_tokens(L, a.segkind, seg, seg_lo, seg_hi);
     const int tok = L.img_start[s] + (c - L.cu_cands[s]);
-    const int nrc = (seg_hi - seg_lo + a.RC - 1) / a.RC;
-    const int rc0 = a.causal ? (tok - seg_lo) / a.RC : 0;
+    const int nrc = chunk_count(seg_hi - seg_lo, a.RC, a.RCF);
+    const int rc0 = a.causal ? chunk_of(tok - seg_lo, seg_hi - seg_lo, a.RC, a.RCF) : 0;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int hb = hg; hb < a.nhb; hb += 8) {
       const float *p = a.partial + (long long)hb * a.RCmax * a.N + c;

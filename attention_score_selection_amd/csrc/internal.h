@@ -55,7 +55,8 @@ struct AttnArgs {
   // column-score kernel
   const float *lse_in;
   float *partial;        // [nhb][RCmax][N]
-  int N, RC, RCmax, KB;  // candidates, row-chunk tokens, max chunks per segment, keys per block
+  int N, RC, RCF;        // candidates, row-chunk tokens, tokens of a piece of the last chunk
+  int RCmax, KB;         // max chunks per segment, keys per block
 };
 
 // Attention forward: the LSE kernel's job split plus the values and output.
@@ -70,11 +71,41 @@ struct FwdArgs {
 // Host-side plan of one attention launch.
 struct AttnPlan {
   int dtype, D, NT;
-  int F, nhb, TB, KB, RC, RCmax;
+  int F, nhb, TB, KB, RC, RCF, RCmax;
   int nseg, segkind;
   long long jobs_per_hb, total_jobs;
   size_t partial_bytes;
 };
+
+// Row chunks of the column score over a segment of n tokens: chunks of RC
+// tokens, except that a segment longer than RC has the range after its last
+// whole chunk cut into pieces of RCF tokens (RCF divides RC; RCF == RC leaves
+// it whole).  The pieces come last in the enumeration, so a launch whose jobs
+// are long ends on short ones.  A segment of at most RC tokens is one chunk.
+__host__ __device__ inline int chunk_whole(int n, int RC) { return n > RC ? (n - 1) / RC : 1; }
+__host__ __device__ inline int chunk_count(int n, int RC, int RCF) {
+  if (n <= 0) return 0;
+  const int whole = chunk_whole(n, RC);
+  const int rest = n - whole * RC;
+  return whole + (rest > 0 ? (rest + RCF - 1) / RCF : 0);
+}
+// Token range [lo, hi) of chunk r, relative to the segment start.
+__host__ __device__ inline void chunk_range(int r, int n, int RC, int RCF, int &lo, int &hi) {
+  const int whole = chunk_whole(n, RC);
+  if (r < whole) {
+    lo = r * RC;
+    hi = lo + RC;
+  } else {
+    lo = whole * RC + (r - whole) * RCF;
+    hi = lo + RCF;
+  }
+  if (hi > n) hi = n;
+}
+// Chunk holding token t (relative to the segment start, 0 <= t < n).
+__host__ __device__ inline int chunk_of(int t, int n, int RC, int RCF) {
+  const int whole = chunk_whole(n, RC);
+  return t < whole * RC ? t / RC : whole + (t - whole * RC) / RCF;
+}
 
 // Error reporting (thread-local message).
 int fail(int code, const char *fmt, ...);

@@ -185,6 +185,24 @@ def test_workspace_sizes_and_shortfall(lib):
     assert rc == B.TSEL_EWORKSPACE
 
 
+def test_colscore_cuts_the_last_chunk_of_long_segments(lib):
+    """Row chunks of 8192 query rows (512 tokens at 16 folded heads); a
+    segment longer than one chunk, in a launch with at least 512 jobs, has
+    the range after its last whole chunk cut into pieces of a quarter chunk,
+    each with its own partial row in the workspace."""
+    # Request 0: 4496 tokens, four 32x32 images; request 1: 300 tokens, one 12x12 image.
+    lay = HostLayout([0, 4496, 4796], [0, 4, 5], [100, 1161, 2185, 3259, 4506],
+                     [[32, 32]] * 4 + [[12, 12]], [0, 1024, 2048, 3072, 4096, 4240])
+    a = attn(dtype=B.TSEL_F32, hq=32, hkv=2, d=128)
+    need = lib.tsel_workspace_size(B.TSEL_OP_COLSCORE, ctypes.byref(a), ctypes.byref(lay.c))
+    # 2 head blocks x (8 whole chunks + 400 tokens in 4 pieces of 128) x 4240 candidates.
+    assert need == 2 * 12 * 4240 * 4
+    # A short layout halves its chunks instead and is never cut.
+    a = attn(dtype=B.TSEL_F32, hq=32, hkv=2, d=128)
+    need = lib.tsel_workspace_size(B.TSEL_OP_COLSCORE, ctypes.byref(a), ctypes.byref(good_layout().c))
+    assert need == 2 * 1 * 22 * 4
+
+
 def test_attention_fwd_validation(lib):
     lay = good_layout()
     f = lib.tsel_attention_fwd

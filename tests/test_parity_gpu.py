@@ -70,6 +70,27 @@ def test_medium_random(dev, i):
                  prob.emb)
 
 
+# One request longer than a row chunk (512 tokens at 16 folded heads) in a
+# launch with enough jobs for full-size chunks, so the column score cuts the
+# range after its last whole chunk (400 tokens) into pieces of 128; a short
+# second request stays one chunk and makes the launch reorder its jobs.
+LONG_SEGMENT = [(4496, [(100, 32, 32), (1161, 32, 32), (2185, 32, 32), (3259, 32, 32)]),
+                (300, [(10, 12, 12)])]
+
+
+@pytest.mark.parametrize("mask", ["causal", "full"])
+def test_long_segment_last_chunk_pieces(dev, mask):
+    prob = make_problem(f"long_segment_pieces_{mask}_f32_h32x2_d128", LONG_SEGMENT, 32, 2, 128, "f32",
+                        mask, 1.0, 61, ratio_range=(0.3, 0.9), emb_dim=16)
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    # 2 head blocks x 12 chunks (8 whole + 4 pieces) x N candidates of fp32.
+    op = tsel.binding.TSEL_OP_COLSCORE
+    assert tsel.tsel_workspace_size(op, lay, prob.q, prob.k, mask) == 2 * 12 * prob.N * 4
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, workers=oracle.default_workers(), with_emb=False), prob.emb)
+
+
 SMALL_FP8 = [("full", 4, 4, 64), ("causal", 8, 2, 128), ("blockdiag", 4, 2, 64), ("causal", 16, 1, 128)]
 
 
