@@ -56,84 +56,125 @@ __device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total) {
   return res;
 }
 
-// Pools of up to kTopkThreads * kTopkRegKeys candidates: every thread holds
-// a contiguous run of at most kTopkRegKeys keys in registers for all passes.
-// Histogram adds are merged per thread while consecutive keys share a digit
-// (the keys of one pool often share their leading digits), and the final
-// ordered admission of keys equal to tau needs one block scan of per-thread
-// counts.
+// Pools of up to kTopkThreads * kTopkRegKeys candidates keep their keys in
+// registers for all passes: key j of thread t is candidate t + 1024 j, so
+// every load and flag store of a wave covers 64 consecutive candidates.
+// Histogram adds are merged per thread while its consecutive keys share a
+// digit (a pool's scores mostly share their leading digits, so unmerged adds
+// would serialise on one address).  Keys equal to tau are admitted in index
+// order, i.e. by (j, wave, lane): ballots count them per (j, wave), one
+// block scan over those counts gives each (j, wave) its offset.
 constexpr int kTopkRegKeys = 32;
+constexpr int kTopkWaves = kTopkThreads / 64;
 
 // known: tau = `known_tau` and `known_kr` keys equal to it are kept (the
-// caller found them already); the descent is skipped.
+// caller found them already); the descent is skipped.  LDS: hist 512 ints,
+// eqbuf RK * 16 ints.
+template <int RK>
 __device__ __forceinline__ void topk_registers(const float *score, int n, int k, uint8_t *keep,
-                                               int *hist, int *sh, int &s_digit, int &s_above,
+                                               int *hist, int *sh, int *eqbuf, int &s_digit, int &s_above,
                                                bool known = false, uint32_t known_tau = 0u,
                                                int known_kr = 0) {
-  const int tid = threadIdx.x;
-  const int per = (n + kTopkThreads - 1) / kTopkThreads;
-  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
-  uint32_t u[kTopkRegKeys];
+  const int tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
+  // Loads from clamped indices without branches, so that all are in flight
+  // at once; keys past the pool are masked out by index below.
+  float f[RK];
 #pragma unroll
-  for (int j = 0; j < kTopkRegKeys; ++j) u[j] = (i0 + j < i1) ? score_key(score[i0 + j]) : 0u;
+  for (int j = 0; j < RK; ++j) f[j] = score[min(tid + kTopkThreads * j, n - 1)];
+  uint32_t u[RK];
+#pragma unroll
+  for (int j = 0; j < RK; ++j) u[j] = score_key(f[j]);
   uint32_t prefix = known ? known_tau : 0u, pmask = 0u;
   int kr = known ? known_kr : k;  // how many of the keys matching `prefix` must still be kept
+  int neq = -1;                   // keys equal to tau, when the descent found it
+  // Two histograms (hist[0..511]) alternate between passes, so clearing the
+  // next one overlaps this pass's digit walk: two barriers per pass.
+  if (!known) {
+    if (tid < 512) hist[tid] = 0;
+    __syncthreads();
+  }
   for (int pass = 0; pass < (known ? 0 : 4); ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+    int *H = hist + 256 * (pass & 1);
     int cur = -1, cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kTopkRegKeys; ++j) {
-      if (i0 + j < i1 && (u[j] & pmask) == prefix) {
+    for (int j = 0; j < RK; ++j) {
+      if (tid + kTopkThreads * j < n && (u[j] & pmask) == prefix) {
         const int d = (int)((u[j] >> shift) & 255u);
         if (d != cur) {
-          if (cnt) atomicAdd(&hist[cur], cnt);
+          if (cnt) atomicAdd(&H[cur], cnt);
           cur = d;
           cnt = 0;
         }
         ++cnt;
       }
     }
-    if (cnt) atomicAdd(&hist[cur], cnt);
+    if (cnt) atomicAdd(&H[cur], cnt);
     __syncthreads();
-    // Suffix counts over digits: scan the histogram from digit 255 down.
-    const int hv = (tid < 256) ? hist[255 - tid] : 0;
-    int tot;
-    const int excl = block_excl_scan(hv, sh, tot);
-    if (tid < 256) {
-      const int above = excl, upto = excl + hv;
-      if (above < kr && upto >= kr) {
-        s_digit = 255 - tid;
-        s_above = above;
+    if (wid == 0) {
+      // Wave 0 walks the digits from 255 down: lane l holds 255-4l .. 252-4l.
+      int c[4], csum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = H[255 - 4 * lane - j];
+        csum += c[j];
       }
+      int cb = wave_incl_scan(csum) - csum;  // keys with a larger digit
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (cb < kr && cb + c[j] >= kr) {
+          s_digit = 255 - 4 * lane - j;
+          s_above = cb;
+          sh[0] = c[j];
+        }
+        cb += c[j];
+      }
+    } else if (tid < 64 + 256) {
+      hist[256 * ((pass + 1) & 1) + tid - 64] = 0;
     }
     __syncthreads();
     kr -= s_above;
     prefix |= (uint32_t)s_digit << shift;
     pmask |= 255u << shift;
-    __syncthreads();
+    if (pass == 3) neq = sh[0];
   }
-  // prefix = tau; the kr lowest-index keys equal to tau are kept.
-  int eq = 0;
+  // prefix = tau; the kr lowest-index keys equal to tau are kept.  When all
+  // of them are (the usual case: ties at tau are rare), no ranks are needed.
+  if (neq == kr) {
 #pragma unroll
-  for (int j = 0; j < kTopkRegKeys; ++j) eq += (i0 + j < i1 && u[j] == prefix) ? 1 : 0;
-  int tot;
-  int rank = block_excl_scan(eq, sh, tot);
-#pragma unroll
-  for (int j = 0; j < kTopkRegKeys; ++j) {
-    if (i0 + j < i1) {
-      const bool e = u[j] == prefix;
-      keep[i0 + j] = (u[j] > prefix || (e && rank < kr)) ? 1 : 0;
-      rank += e ? 1 : 0;
+    for (int j = 0; j < RK; ++j) {
+      const int i = tid + kTopkThreads * j;
+      if (i < n) keep[i] = (u[j] >= prefix) ? 1 : 0;
     }
+    return;
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < RK; ++j) {
+    const unsigned long long m = __ballot(tid + kTopkThreads * j < n && u[j] == prefix);
+    if (lane == 0) eqbuf[j * kTopkWaves + wid] = __popcll(m);
+  }
+  __syncthreads();
+  int tot;
+  const int cv = (tid < RK * kTopkWaves) ? eqbuf[tid] : 0;
+  const int cx = block_excl_scan(cv, sh, tot);
+  if (tid < RK * kTopkWaves) eqbuf[tid] = cx;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < RK; ++j) {
+    const int i = tid + kTopkThreads * j;
+    const bool e = i < n && u[j] == prefix;
+    const unsigned long long m = __ballot(e);
+    const int rank = eqbuf[j * kTopkWaves + wid] + __popcll(m & below);
+    if (i < n) keep[i] = (u[j] > prefix || (e && rank < kr)) ? 1 : 0;
   }
 }
 
 // Keep flags of one pool of n candidates: the k largest keys, equal keys by
 // ascending index.  Every thread of the 1024-thread block calls it.
-__device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint8_t *keep, int *hist, int *sh, int &s_digit,
-                          int &s_above, bool known = false, uint32_t known_tau = 0u, int known_kr = 0) {
+__device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint8_t *keep, int *hist, int *sh,
+                                          int *eqbuf, int &s_digit, int &s_above, bool known = false,
+                                          uint32_t known_tau = 0u, int known_kr = 0) {
   const int tid = threadIdx.x;
   if (n <= 0) return;
   if (k <= 0 || k >= n) {
@@ -142,7 +183,12 @@ __device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint
     return;
   }
   if (n <= kTopkThreads * kTopkRegKeys) {
-    topk_registers(score, n, k, keep, hist, sh, s_digit, s_above, known, known_tau, known_kr);
+    // Register runs sized to the pool: short runs skip the empty iterations.
+    const int per = (n + kTopkThreads - 1) / kTopkThreads;
+    if (per <= 1) topk_registers<1>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
+    else if (per <= 4) topk_registers<4>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
+    else if (per <= 16) topk_registers<16>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
+    else topk_registers<kTopkRegKeys>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
     return;
   }
   uint32_t prefix = known ? known_tau : 0u, pmask = 0u;
@@ -190,13 +236,14 @@ __device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const float *score,
                                                            TopkChunk ks, uint8_t *keep) {
-  __shared__ int hist[256];
+  __shared__ int hist[512];
   __shared__ int sh[17];
+  __shared__ int eqbuf[kTopkRegKeys * kTopkWaves];
   __shared__ int s_digit, s_above;
   const int b = ks.b0 + blockIdx.x;
   const int lo = L.cu_cands[L.cu_images[b]];
   const int hi = L.cu_cands[L.cu_images[b + 1]];
-  topk_pool(score + lo, hi - lo, ks.k[blockIdx.x], keep + lo, hist, sh, s_digit, s_above);
+  topk_pool(score + lo, hi - lo, ks.k[blockIdx.x], keep + lo, hist, sh, eqbuf, s_digit, s_above);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,8 +292,9 @@ __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long l
 
 __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, const float *score, MassChunk mc,
                                                                   int *k_out, uint8_t *keep) {
-  __shared__ int hist[256];
+  __shared__ int hist[512];  // 256 for the mass descent; the top-k alternates two halves
   __shared__ int sh[17];
+  __shared__ int eqbuf[kTopkRegKeys * kTopkWaves];
   __shared__ int s_digit, s_above;
   __shared__ unsigned long long hmass[256];
   __shared__ unsigned long long s_target, s_mabove;
@@ -257,15 +305,21 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
   const int tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
   const float *sc = score + lo;
   // Pools of up to kTopkThreads * kTopkRegKeys candidates keep their keys in
-  // registers, a contiguous run per thread, and merge histogram adds while
-  // consecutive keys share a digit (the leading digits of a pool's scores
-  // are mostly equal, so unmerged adds would serialise on one address).
+  // registers as the top-k does (key j of thread t is candidate t + 1024 j)
+  // and merge histogram adds while a thread's consecutive keys share a digit.
   const bool regs = n <= kTopkThreads * kTopkRegKeys;
-  const int per = (n + kTopkThreads - 1) / kTopkThreads;
-  const int i0 = regs ? min(n, tid * per) : 0, i1 = regs ? min(n, i0 + per) : 0;
+  const int nr = regs ? n : 0;
   uint32_t u[kTopkRegKeys];
+  if (nr > 0) {  // loads from clamped indices, all in flight at once
+    float f[kTopkRegKeys];
 #pragma unroll
-  for (int j = 0; j < kTopkRegKeys; ++j) u[j] = (i0 + j < i1) ? score_key(sc[i0 + j]) : 0u;
+    for (int j = 0; j < kTopkRegKeys; ++j) f[j] = sc[min(tid + kTopkThreads * j, nr - 1)];
+#pragma unroll
+    for (int j = 0; j < kTopkRegKeys; ++j) u[j] = score_key(f[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTopkRegKeys; ++j) u[j] = 0u;
+  }
 
   uint32_t prefix = 0u, pmask = 0u;
   unsigned long long R = 0ull;  // mass still to cover among keys matching `prefix`
@@ -288,7 +342,7 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
       unsigned long long ms = 0ull;
 #pragma unroll
       for (int j = 0; j < kTopkRegKeys; ++j) {
-        if (i0 + j < i1 && (u[j] & pmask) == prefix) {
+        if (tid + kTopkThreads * j < nr && (u[j] & pmask) == prefix) {
           const int d = (int)((u[j] >> shift) & 255u);
           if (d != cur) {
             if (cnt) {
@@ -381,7 +435,7 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
   const int k = s_k;
   // Unclamped and inside the pool: reuse the threshold; otherwise select anew.
   const bool known = need > 0 && k == kstar && k < n;
-  topk_pool(sc, n, k, keep + lo, hist, sh, s_digit, s_above, known, prefix, need);
+  topk_pool(sc, n, k, keep + lo, hist, sh, eqbuf, s_digit, s_above, known, prefix, need);
 }
 
 // Keep decision of token t: text tokens stay, candidates follow their flag.
@@ -431,8 +485,14 @@ __global__ __launch_bounds__(kCompactBlock) void compact_scan(CompactArgs c) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int s = wid; s < c.L.S; s += kCompactBlock / 64) {
       const int c0 = c.L.cu_cands[s], c1 = c.L.cu_cands[s + 1];
-      int cnt = 0;
-      for (int i = c0 + lane; i < c1; i += 64) cnt += c.keep[i] ? 1 : 0;
+      int cnt = 0, i = c0 + lane;
+      for (; i + 448 < c1; i += 512) {  // eight independent loads in flight
+        int t = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t += c.keep[i + 64 * j] ? 1 : 0;
+        cnt += t;
+      }
+      for (; i < c1; i += 64) cnt += c.keep[i] ? 1 : 0;
       cnt = wave_sum(cnt);
       if (lane == 0) c.out_img_counts[s] = cnt;
     }
