@@ -68,13 +68,14 @@ constexpr int kTopkRegKeys = 32;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
 // known: tau = `known_tau` and `known_kr` keys equal to it are kept (the
-// caller found them already); the descent is skipped.  LDS: hist 512 ints,
+// caller found them already, and that the pool holds `known_neq` keys equal
+// to tau, or -1); the descent is skipped.  LDS: hist 512 ints,
 // eqbuf RK * 16 ints.
 template <int RK>
 __device__ __forceinline__ void topk_registers(const float *score, int n, int k, uint8_t *keep,
                                                int *hist, int *sh, int *eqbuf, int &s_digit, int &s_above,
                                                bool known = false, uint32_t known_tau = 0u,
-                                               int known_kr = 0) {
+                                               int known_kr = 0, int known_neq = -1) {
   const int tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
   // Loads from clamped indices without branches, so that all are in flight
   // at once; keys past the pool are masked out by index below.
@@ -86,7 +87,7 @@ __device__ __forceinline__ void topk_registers(const float *score, int n, int k,
   for (int j = 0; j < RK; ++j) u[j] = score_key(f[j]);
   uint32_t prefix = known ? known_tau : 0u, pmask = 0u;
   int kr = known ? known_kr : k;  // how many of the keys matching `prefix` must still be kept
-  int neq = -1;                   // keys equal to tau, when the descent found it
+  int neq = known ? known_neq : -1;  // keys equal to tau, when known (-1: not known)
   // Two histograms (hist[0..511]) alternate between passes, so clearing the
   // next one overlaps this pass's digit walk: two barriers per pass.
   if (!known) {
@@ -174,7 +175,7 @@ __device__ __forceinline__ void topk_registers(const float *score, int n, int k,
 // ascending index.  Every thread of the 1024-thread block calls it.
 __device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint8_t *keep, int *hist, int *sh,
                                           int *eqbuf, int &s_digit, int &s_above, bool known = false,
-                                          uint32_t known_tau = 0u, int known_kr = 0) {
+                                          uint32_t known_tau = 0u, int known_kr = 0, int known_neq = -1) {
   const int tid = threadIdx.x;
   if (n <= 0) return;
   if (k <= 0 || k >= n) {
@@ -185,10 +186,14 @@ __device__ __forceinline__ void topk_pool(const float *score, int n, int k, uint
   if (n <= kTopkThreads * kTopkRegKeys) {
     // Register runs sized to the pool: short runs skip the empty iterations.
     const int per = (n + kTopkThreads - 1) / kTopkThreads;
-    if (per <= 1) topk_registers<1>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
-    else if (per <= 4) topk_registers<4>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
-    else if (per <= 16) topk_registers<16>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
-    else topk_registers<kTopkRegKeys>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr);
+    if (per <= 1) topk_registers<1>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr,
+                                           known_neq);
+    else if (per <= 4) topk_registers<4>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr,
+                                           known_neq);
+    else if (per <= 16) topk_registers<16>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr,
+                                           known_neq);
+    else topk_registers<kTopkRegKeys>(score, n, k, keep, hist, sh, eqbuf, s_digit, s_above, known, known_tau, known_kr,
+                                           known_neq);
     return;
   }
   uint32_t prefix = known ? known_tau : 0u, pmask = 0u;
@@ -292,12 +297,13 @@ __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long l
 
 __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, const float *score, MassChunk mc,
                                                                   int *k_out, uint8_t *keep) {
-  __shared__ int hist[512];  // 256 for the mass descent; the top-k alternates two halves
+  __shared__ int hist[512];  // two count histograms, alternating between passes
   __shared__ int sh[17];
   __shared__ int eqbuf[kTopkRegKeys * kTopkWaves];
   __shared__ int s_digit, s_above;
-  __shared__ unsigned long long hmass[256];
-  __shared__ unsigned long long s_target, s_mabove;
+  __shared__ unsigned long long hmass[512];  // two mass histograms, likewise
+  __shared__ unsigned long long s_target, s_mabove, s_mstar;
+  __shared__ int s_neq;
   __shared__ int s_k;
   const int b = mc.b0 + blockIdx.x;
   const int lo = L.cu_cands[L.cu_images[b]];
@@ -324,15 +330,19 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
   uint32_t prefix = 0u, pmask = 0u;
   unsigned long long R = 0ull;  // mass still to cover among keys matching `prefix`
   unsigned long long mstar = 0ull;
-  int kstar = 0;
+  int kstar = 0, neq = -1;
+  // Two count and mass histograms alternate between passes (wave 0 walks one
+  // while the other waves clear the other): two barriers per pass.
+  if (tid < 512) {
+    hist[tid] = 0;
+    hmass[tid] = 0ull;
+  }
+  __syncthreads();
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) {
-      hist[tid] = 0;
-      hmass[tid] = 0ull;
-    }
-    __syncthreads();
+    int *H = hist + 256 * (pass & 1);
+    unsigned long long *M = hmass + 256 * (pass & 1);
     if (regs) {
       // (Recompute the masses every pass: kept across passes they would take
       // 64 more registers per thread.)
@@ -346,8 +356,8 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
           const int d = (int)((u[j] >> shift) & 255u);
           if (d != cur) {
             if (cnt) {
-              atomicAdd(&hist[cur], cnt);
-              if (ms) atomicAdd(&hmass[cur], ms);
+              atomicAdd(&H[cur], cnt);
+              if (ms) atomicAdd(&M[cur], ms);
             }
             cur = d;
             cnt = 0;
@@ -358,65 +368,73 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
         }
       }
       if (cnt) {
-        atomicAdd(&hist[cur], cnt);
-        if (ms) atomicAdd(&hmass[cur], ms);
+        atomicAdd(&H[cur], cnt);
+        if (ms) atomicAdd(&M[cur], ms);
       }
     } else {
       for (int i = tid; i < n; i += kTopkThreads) {
         const uint32_t v = score_key(sc[i]);
         if ((v & pmask) == prefix) {
           const int d = (int)((v >> shift) & 255u);
-          atomicAdd(&hist[d], 1);
+          atomicAdd(&H[d], 1);
           const unsigned long long m = key_mass(v);
-          if (m) atomicAdd(&hmass[d], m);
+          if (m) atomicAdd(&M[d], m);
         }
       }
     }
     __syncthreads();
-    if (pass == 0) {
-      // The first histogram covers the whole pool: total mass and target.
-      if (tid == 0) {
-        unsigned long long total = 0ull;
-        for (int d = 0; d < 256; ++d) total += hmass[d];
+    if (wid == 0) {
+      // Wave 0 walks the digits from 255 down: lane l holds 255-4l .. 252-4l.
+      unsigned long long mj[4], msum = 0ull;
+      int cj[4], csum = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mj[j] = M[255 - 4 * lane - j];
+        cj[j] = H[255 - 4 * lane - j];
+        msum += mj[j];
+        csum += cj[j];
+      }
+      unsigned long long mb = wave_incl_scan_u64(msum);  // inclusive for now
+      unsigned long long Rw = R;
+      if (pass == 0) {
+        // The first histogram covers the whole pool: total mass and target.
+        const unsigned long long total = __shfl(mb, 63, 64);
         const double x = ceil((mc.tau[blockIdx.x] * (double)total) * (1.0 - 1e-12));
         const unsigned long long tg = (unsigned long long)x;
-        s_target = tg < total ? tg : total;
+        Rw = tg < total ? tg : total;
+        if (lane == 0) s_target = Rw;
       }
-      __syncthreads();
-      R = s_target;
-      if (R == 0ull) break;  // uniform across the block
-    }
-    // Wave 0 walks the digits from 255 down: lane l holds digits 255-4l .. 252-4l.
-    if (wid == 0) {
-      unsigned long long msum = 0ull;
-      int csum = 0;
+      mb -= msum;                                // mass of larger digits
+      int cb = wave_incl_scan(csum) - csum;      // count of larger digits
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        msum += hmass[255 - 4 * lane - j];
-        csum += hist[255 - 4 * lane - j];
-      }
-      unsigned long long mb = wave_incl_scan_u64(msum) - msum;  // mass of larger digits
-      int cb = wave_incl_scan(csum) - csum;                    // count of larger digits
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned long long mj = hmass[255 - 4 * lane - j];
-        if (mb < R && mb + mj >= R) {
+        if (mb < Rw && mb + mj[j] >= Rw) {
           s_digit = 255 - 4 * lane - j;
           s_above = cb;
           s_mabove = mb;
+          s_mstar = cj[j] ? mj[j] / (unsigned long long)cj[j] : 0ull;  // last pass: one key, one mass
+          s_neq = cj[j];                                               // ... and its count
         }
-        mb += mj;
-        cb += hist[255 - 4 * lane - j];
+        mb += mj[j];
+        cb += cj[j];
       }
+    } else if (tid < 64 + 256) {
+      hist[256 * ((pass + 1) & 1) + tid - 64] = 0;
+      hmass[256 * ((pass + 1) & 1) + tid - 64] = 0ull;
     }
     __syncthreads();
-    const int d = s_digit;
+    if (pass == 0) {
+      R = s_target;
+      if (R == 0ull) break;  // uniform across the block
+    }
     R -= s_mabove;
     kstar += s_above;
-    prefix |= (uint32_t)d << shift;
+    prefix |= (uint32_t)s_digit << shift;
     pmask |= 255u << shift;
-    if (pass == 3) mstar = hmass[d] / (unsigned long long)hist[d];  // one key: one mass
-    __syncthreads();
+    if (pass == 3) {
+      mstar = s_mstar;
+      neq = s_neq;
+    }
   }
   // R > 0 here only if the descent ran: the candidates of key `prefix` (each
   // of mass mstar) complete the target, and the k*-th largest key is
@@ -435,7 +453,7 @@ __global__ __launch_bounds__(kTopkThreads) void mass_budget_kernel(DevLayout L, 
   const int k = s_k;
   // Unclamped and inside the pool: reuse the threshold; otherwise select anew.
   const bool known = need > 0 && k == kstar && k < n;
-  topk_pool(sc, n, k, keep + lo, hist, sh, eqbuf, s_digit, s_above, known, prefix, need);
+  topk_pool(sc, n, k, keep + lo, hist, sh, eqbuf, s_digit, s_above, known, prefix, need, neq);
 }
 
 // Keep decision of token t: text tokens stay, candidates follow their flag.
