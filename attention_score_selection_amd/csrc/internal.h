@@ -146,6 +146,7 @@ struct CompactArgs {
   int N;
   int nblk;
   int *blk_cnt, *blk_off, *total;  // workspace
+  int fused;                        // 1: the scatter forms the block offsets and image counts itself
   int cap;
   int *out_token_idx, *out_spatial, *out_cu_seqlens, *out_img_counts;
 };

@@ -479,6 +479,10 @@ __global__ __launch_bounds__(kCompactBlock) void compact_count(CompactArgs c) {
   int tot;
   block_excl_scan(k, sh, tot);
   if (threadIdx.x == 0) c.blk_cnt[blockIdx.x] = tot;
+  // Fused path: the scatter adds the per-image counts up, so clear them here.
+  if (c.fused && c.out_img_counts != nullptr)
+    for (int i = blockIdx.x * kCompactBlock + threadIdx.x; i < c.L.S; i += gridDim.x * kCompactBlock)
+      c.out_img_counts[i] = 0;
 }
 
 // One block: offsets of the token blocks, the total, trailing empty requests,
@@ -517,13 +521,45 @@ __global__ __launch_bounds__(kCompactBlock) void compact_scan(CompactArgs c) {
   }
 }
 
+// Fused path (c.fused): every block sums the counts of the blocks before it
+// (a few dozen for the usual sizes), the last block writes the total and the
+// trailing requests, and each wave adds its kept image tokens to their
+// images' counts, one integer atomic per (wave, image).
 __global__ __launch_bounds__(kCompactBlock) void compact_scatter(CompactArgs c) {
   __shared__ int sh[17];
+  __shared__ int s_base;
   const int t = blockIdx.x * kCompactBlock + threadIdx.x;
   int s = -1, off = 0;
   const int k = (t < c.L.T) ? token_keep(c.L, c.keep, t, s, off) : 0;
+  if (c.fused && threadIdx.x < 64) {
+    int v = 0;
+    for (int i = threadIdx.x; i < (int)blockIdx.x; i += 64) v += c.blk_cnt[i];
+    v = wave_sum(v);
+    if (threadIdx.x == 0) s_base = v;
+  }
   int tot;
-  const int pos = c.blk_off[blockIdx.x] + block_excl_scan(k, sh, tot);
+  const int ex = block_excl_scan(k, sh, tot);  // its barriers also publish s_base
+  const int base = c.fused ? s_base : c.blk_off[blockIdx.x];
+  const int pos = base + ex;
+  if (c.fused) {
+    if (blockIdx.x == gridDim.x - 1) {
+      if (threadIdx.x == 0) *c.total = base + tot;
+      if (c.out_cu_seqlens != nullptr)
+        for (int b = threadIdx.x; b <= c.L.B; b += kCompactBlock)
+          if (c.L.cu_seqlens[b] == c.L.T) c.out_cu_seqlens[b] = base + tot;
+    }
+    if (c.out_img_counts != nullptr) {
+      const bool mine = k && s >= 0;
+      unsigned long long m = __ballot(mine);
+      while (m) {  // wave-uniform
+        const int l0 = __ffsll((long long)m) - 1;
+        const int s0 = __shfl(s, l0, 64);
+        const unsigned long long same = __ballot(mine && s == s0);
+        if (lane_id() == l0) atomicAdd(&c.out_img_counts[s0], (int)__popcll(same));
+        m &= ~same;
+      }
+    }
+  }
   if (t >= c.L.T) return;
   if (k && pos < c.cap) {
     c.out_token_idx[pos] = t;
@@ -646,11 +682,18 @@ hipError_t launch_mass_budget(const DevLayout &L, const float *score, const Mass
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const CompactArgs &c, hipStream_t s) {
+// Up to kCompactFusedBlocks token blocks (4M tokens) the scatter forms its
+// own offsets (two launches); beyond, and for an empty layout, a one-block
+// scan runs between count and scatter.
+constexpr int kCompactFusedBlocks = 4096;
+
+hipError_t launch_compact(const CompactArgs &args, hipStream_t s) {
+  CompactArgs c = args;
+  c.fused = (c.nblk > 0 && c.nblk <= kCompactFusedBlocks) ? 1 : 0;
   if (c.nblk > 0) {
     hipLaunchKernelGGL(compact_count, dim3(c.nblk), dim3(kCompactBlock), 0, s, c);
   }
-  hipLaunchKernelGGL(compact_scan, dim3(1), dim3(kCompactBlock), 0, s, c);
+  if (!c.fused) hipLaunchKernelGGL(compact_scan, dim3(1), dim3(kCompactBlock), 0, s, c);
   if (c.nblk > 0) {
     hipLaunchKernelGGL(compact_scatter, dim3(c.nblk), dim3(kCompactBlock), 0, s, c);
   }

@@ -413,11 +413,13 @@ def _token_tables(prob):
     return cand, img
 
 
-def compact(prob, keep: np.ndarray, emb=None):
+def compact(prob, keep: np.ndarray, emb=None, with_positions: bool = True):
     """Stable compaction (numpy).  Returns a dict with ``token_idx`` [T_out],
     ``spatial`` [T_out, 3] ((img, row, col), -1 for text), ``cu_seqlens``
-    [B+1], ``img_counts`` [S] and, when ``emb`` is given, ``emb`` [T_out, D]
-    (a row copy, bit-exact)."""
+    [B+1], ``img_counts`` [S], the rotary ``positions`` [T_out, 3] of the
+    kept tokens (unless ``with_positions`` is false: a token-by-token loop,
+    slow for millions of tokens) and, when ``emb`` is given, ``emb``
+    [T_out, D] (a row copy, bit-exact)."""
     cand, img = _token_tables(prob)
     if prob.N == 0:
         keep_tok = np.ones(prob.T, bool)
@@ -440,7 +442,8 @@ def compact(prob, keep: np.ndarray, emb=None):
                cu_seqlens=cu_out.astype(np.int64), img_counts=img_counts)
     if emb is not None:
         out["emb"] = emb[token_idx]
-    out["positions"] = rope_positions(prob)[token_idx]
+    if with_positions:
+        out["positions"] = rope_positions(prob)[token_idx]
     return out
 
 

@@ -91,6 +91,51 @@ def test_long_segment_last_chunk_pieces(dev, mask):
     P.full_check(prob, got, oracle.run(prob, workers=oracle.default_workers(), with_emb=False), prob.emb)
 
 
+def layout_only(seed, t_target, n_req=3):
+    """A layout of about t_target tokens (images of 64-128 rows and columns
+    with text between them), without Q/K: for the compaction alone."""
+    rng = np.random.default_rng(seed)
+    seqlens, starts, hw = [0], [], []
+    per = t_target // n_req
+    for _ in range(n_req):
+        t = seqlens[-1] + 37
+        while t < seqlens[-1] + per:
+            h, w = (int(x) for x in rng.integers(64, 129, size=2))
+            starts.append(t)
+            hw.append((h, w))
+            t += h * w + int(rng.integers(0, 51))
+        seqlens.append(t + 11)
+    cu_images = [0]
+    for b in range(n_req):
+        cu_images.append(sum(1 for x in starts if x < seqlens[b + 1]))
+    hw = np.array(hw, np.int64)
+    cu_cands = np.concatenate([[0], np.cumsum(hw[:, 0] * hw[:, 1])])
+    from types import SimpleNamespace
+    return SimpleNamespace(T=seqlens[-1], B=n_req, S=len(starts), N=int(cu_cands[-1]),
+                           cu_seqlens=np.array(seqlens, np.int64), cu_images=np.array(cu_images, np.int64),
+                           img_start=np.array(starts, np.int64), img_hw=hw, cu_cands=cu_cands)
+
+
+@pytest.mark.parametrize("t_target", [300_000, 4_300_000])
+def test_compaction_alone_at_block_count_limits(dev, t_target):
+    """tsel_compact alone on random keep flags: ~300 token blocks of 1024
+    (the scatter pass forms its own block offsets and image counts) and over
+    4096 blocks (a one-block scan between count and scatter forms them)."""
+    lay_np = layout_only(70 + t_target % 7, t_target)
+    print(f"\n[case] compaction alone T={lay_np.T} S={lay_np.S} N={lay_np.N}", flush=True)
+    keep = (np.random.default_rng(71).random(lay_np.N) < 0.6).astype(np.uint8)
+    lay = tsel.Layout(lay_np.cu_seqlens, lay_np.cu_images, lay_np.img_start, lay_np.img_hw, lay_np.cu_cands, dev)
+    kb = [int(keep[lay_np.cu_cands[lay_np.cu_images[b]]:lay_np.cu_cands[lay_np.cu_images[b + 1]]].sum())
+          for b in range(lay_np.B)]
+    out = tsel.tsel_compact(lay, torch.from_numpy(keep).to(dev), kb)
+    torch.cuda.synchronize(dev)
+    ref = oracle.compact(lay_np, keep, with_positions=False)
+    assert np.array_equal(out["token_idx"].cpu().numpy(), ref["token_idx"])
+    assert np.array_equal(out["spatial"].cpu().numpy(), ref["spatial"])
+    assert np.array_equal(out["cu_seqlens"].cpu().numpy(), ref["cu_seqlens"])
+    assert np.array_equal(out["img_counts"].cpu().numpy()[: lay_np.S], ref["img_counts"])
+
+
 SMALL_FP8 = [("full", 4, 4, 64), ("causal", 8, 2, 128), ("blockdiag", 4, 2, 64), ("causal", 16, 1, 128)]
 
 
