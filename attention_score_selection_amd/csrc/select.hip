@@ -4,18 +4,20 @@
 // 1024-thread workgroup per pool runs an exact MSB-first radix select on
 // order-preserving 32-bit keys of the fp32 scores (four 8-bit digits, integer
 // LDS histograms), which yields the k-th largest key tau and how many keys
-// equal to tau still fit; a block-wide ordered scan then admits those equal
-// keys by ascending candidate index.  No floating-point atomics: the result
-// is exact and deterministic.  The input-dependent budget reuses that
+// equal to tau still fit; those equal keys are then admitted by ascending
+// candidate index.  No floating-point atomics: the result is exact and
+// deterministic.  The input-dependent budget reuses that
 // descent with integer mass histograms to find how many candidates a pool
 // keeps (the REDtech article's section 6.2 names choosing the rate from the
 // input; the mass-coverage rule is this library's reading).
 //
 // Compaction (new lengths, image boundaries and original spatial indices,
-// REDtech article section 3.2): per-block keep counts, one scan block, then a
-// scatter pass that recomputes each token's flag and writes its original
-// index and (image, row, col); a separate gather copies embedding rows with
-// 16-byte vector loads.
+// REDtech article section 3.2): per-block keep counts, then a scatter pass
+// that forms each block's offset from those counts, recomputes each token's
+// flag and writes its original index and (image, row, col), plus the image
+// counts (integer atomics); very long layouts put a one-block scan between
+// the two.  A separate gather copies embedding rows with 16-byte vector
+// loads.
 #include <type_traits>
 
 #include "device.h"
