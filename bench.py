@@ -108,6 +108,29 @@ def cpu_baseline(prob, elems_per_head, budget_s=10.0):
                       f"({done} KV group(s), {elems:.4g} elements) of the same workload, {dt:.1f} s"}
 
 
+def budget_competition(prob, outs):
+    """Kept fraction of the images with dominant keys against the others in
+    one global pool (the REDtech article's multi-image budget competition:
+    detail-dense images keep more tokens).  Reported, not a target: the
+    synthetic populations stand in for the article's image sets."""
+    import numpy as np
+    if prob.S < 2 or len(prob.dominant) == 0:
+        return None
+    img_of = np.full(prob.T, -1, np.int64)
+    for s in range(prob.S):
+        n = int(prob.img_hw[s, 0] * prob.img_hw[s, 1])
+        img_of[prob.img_start[s]:prob.img_start[s] + n] = s
+    dom_imgs = set(int(x) for x in img_of[prob.dominant] if x >= 0)
+    if not dom_imgs or len(dom_imgs) == prob.S:
+        return None
+    counts = outs["img_counts"][: prob.S].cpu().numpy().astype(np.float64)
+    sizes = (prob.img_hw[:, 0] * prob.img_hw[:, 1]).astype(np.float64)
+    frac = counts / sizes
+    dom = np.array([s in dom_imgs for s in range(prob.S)])
+    return {"images_with_dominant_keys": int(dom.sum()), "other_images": int((~dom).sum()),
+            "kept_fraction_dominant": float(frac[dom].mean()), "kept_fraction_other": float(frac[~dom].mean())}
+
+
 def time_forward(tsel, prob, q, k, lay, dev, stream, args, peak, lse_elems):
     """The layer's attention forward (O and LSE) timed with HIP events;
     4*d flops per visible (head, row, key) pair (QK^T and PV)."""
@@ -329,6 +352,9 @@ def main():
         gev[1].record(stream)
         torch.cuda.synchronize(dev)
         result["graph_replay"] = {"ms_per_step": gev[0].elapsed_time(gev[1]) / args.steps}
+    comp = budget_competition(prob, outs)
+    if comp is not None:
+        result["budget_competition"] = comp
     if args.mass_tau is not None:
         result["budget_mass"] = time_mass(tsel, prob, score, lay, dev, stream, args)
     if args.calib_copy_mb > 0:
