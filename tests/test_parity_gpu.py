@@ -473,9 +473,10 @@ def test_deterministic_repeat(dev):
 @pytest.mark.parametrize("pattern", ["distinct", "ties", "nonfinite"])
 def test_budget_topk_synthetic_scores_all_pool_sizes(dev, pattern):
     """tsel_budget_topk alone on synthetic fp32 scores (drawn here, not by the
-    GPU path), pools on both sides of the register-resident limit (32768)
-    and past it, against the oracle's rank rule exactly."""
-    sizes = [5, 1000, 1023, 32768, 32769, 50000]
+    GPU path), pools on both sides of every register-run size (1, 4, 16 and 32
+    keys per thread: pool limits 1024, 4096, 16384, 32768) and past the last
+    into the streaming path, against the oracle's rank rule exactly."""
+    sizes = [5, 1000, 1023, 1024, 1025, 3000, 4096, 4097, 9000, 16384, 16385, 32768, 32769, 50000]
     reqs, off = [], 0
     for n in sizes:
         side = int(np.ceil(np.sqrt(n)))
