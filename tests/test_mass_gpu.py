@@ -50,8 +50,9 @@ def pools_problem(sizes, name, seed):
 
 @pytest.mark.parametrize("pattern", ["diffuse", "peaked", "ties", "nonfinite", "above_one"])
 def test_budget_mass_synthetic_pools(dev, pattern):
-    """Pools on both sides of the register-resident top-k limit (32768)."""
-    sizes = [5, 1000, 1023, 32768, 32769, 50000]
+    """Pools on both sides of every register-run size of the top-k admission
+    (1024, 4096, 16384 and 32768 candidates) and past the last."""
+    sizes = [5, 1000, 1023, 1025, 4096, 4097, 16385, 32768, 32769, 50000]
     prob = pools_problem(sizes, "mass_pools_" + pattern, 41)
     rng = np.random.default_rng(42)
     parts = []
