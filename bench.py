@@ -102,7 +102,14 @@ def cpu_baseline(prob, elems_per_head, budget_s=10.0):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
     except OSError:
         pass
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        visible = os.cpu_count() or 1
     return {"value": elems / dt, "unit": "score elements/s", "cores": workers, "kind": "oracle",
+            "cores_visible": visible,
+            "cores_note": "threads = the cores this process may run on, capped at 16: the host's CPU "
+                          "share of one GPU on this machine class",
             "cpu_model": model,
             "sample": f"fp64 LSE + column mass of query heads 0-{done * hg - 1} "
                       f"({done} KV group(s), {elems:.4g} elements) of the same workload, {dt:.1f} s"}
@@ -178,6 +185,31 @@ def time_mass(tsel, prob, score, lay, dev, stream, args):
             "GBps": 5.0 * prob.N / t / 1e9}
 
 
+def time_gemm(n, dev, stream, args):
+    """A dense bf16 n x n x n product through torch.matmul (hipBLASLt) on
+    normal random operands, timed with HIP events: a reference for the MFMA
+    rate, and the clock it runs at, that a tuned dense kernel reaches here."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    for _ in range(max(args.warmup, 3)):
+        torch.matmul(a, b, out=c)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = max(args.steps, 10)
+    ev[0].record(stream)
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    ev[1].record(stream)
+    torch.cuda.synchronize(dev)
+    t = ev[0].elapsed_time(ev[1]) / 1e3 / reps
+    tf = 2.0 * n ** 3 / t / 1e12
+    return {"n": n, "ms": t * 1e3, "tflops": tf, "frac": tf / PEAK_TFLOPS["bf16"],
+            "library": "torch.matmul (hipBLASLt), bf16 in and out, fp32 accumulate"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +218,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
+    ap.add_argument("--calib-gemm", type=int, default=0,
+                    help="also time a plain n x n x n bf16 matrix product (torch.matmul, i.e. the "
+                         "vendor GEMM library) on random data: the MFMA rate a dense library "
+                         "kernel sustains on this GPU")
     ap.add_argument("--forward", action="store_true",
                     help="also time the attention forward (tsel_attention_fwd) on the same layer")
     ap.add_argument("--cold", action="store_true",
@@ -365,6 +401,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize(dev)
         result["calib_copy_bytes"] = n
+    if args.calib_gemm > 0:
+        result["calib_gemm"] = time_gemm(args.calib_gemm, dev, stream, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prob, col_elems / prob.hq)
     print(json.dumps(result), flush=True)

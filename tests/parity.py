@@ -11,11 +11,19 @@ Tolerances (written here, used by every GPU test):
   does not hide relative errors of tiny scores.
 * LSE: |gpu - oracle| <= 1e-4 (bf16/f16/fp8) or 1e-5 (fp32), absolute,
   natural log units.
-* kept sets: exact, except inside the tie band of a pool: with oracle masses
-  sorted descending and tau = max(rtol * m_(k), 1e-6), if m_(k) - m_(k+1) <=
-  4 tau then the candidates with m_(k+1) - 2 tau <= m <= m_(k) + 2 tau may be
-  chosen freely (the count must still be k); everything above the band must
-  be kept and everything below it dropped.
+* kept sets: exact, except inside the tie band of a pool.  With oracle
+  masses m sorted descending, m_(k) the k-th and m_(k+1) the (k+1)-th, let
+  tau = max(rtol * m_(k) / (1 - 2 rtol), 1e-6).  A GPU mass g_j passes the
+  mass test when |g_j - m_j| <= t_j = max(rtol * m_j, 1e-6), and t_j <= tau
+  for every m_j <= m_(k) + 2 tau.  Then
+    - m_j > m_(k+1) + 2 tau: g_j > m_(k+1) + tau >= g_i for each of the
+      n - k candidates i with m_i <= m_(k+1), so j is kept by any such GPU;
+    - m_j < m_(k) - 2 tau: g_j < m_(k) - tau <= g_i for each of the k
+      candidates i with m_i >= m_(k), so j is dropped by any such GPU.
+  Only candidates with m_(k) - 2 tau <= m_j <= m_(k+1) + 2 tau may be chosen
+  freely (the count must still be k); that band holds candidates only when
+  m_(k) - m_(k+1) <= 2 tau, the widest gap the score tolerance can explain.
+  Everything outside it must match the oracle's kept set exactly.
 * compaction, gather and rotary positions: bit-exact against the oracle's
   compaction of the oracle's flags whenever the kept sets agree; otherwise
   checked for validity against the GPU's own flags (order, bounds, spatial
@@ -98,17 +106,31 @@ def check_keep(prob, gpu_keep, ref_mass, ks, pools=None):
         m = np.where(np.isfinite(ref_mass[lo:hi]), ref_mass[lo:hi], -np.inf)
         ref_keep = np.zeros(n, bool)
         ref_keep[np.lexsort((np.arange(n), -m))[:k]] = True
-        srt = np.sort(m)[::-1]
-        mk, mk1 = srt[k - 1], srt[k]
-        tau = max(rtol * abs(mk), 1e-6)
-        if np.isfinite(mk) and np.isfinite(mk1) and mk - mk1 <= 4 * tau:
-            band = (m >= mk1 - 2 * tau) & (m <= mk + 2 * tau)
+        band = tie_band(m, k, rtol)
+        if band.any():
+            print(f"[tie band] {prob.name} pool {b}: {int(band.sum())} of {n} candidates free "
+                  f"(k = {k})", flush=True)
             assert np.array_equal(g[~band], ref_keep[~band]), f"{prob.name}: pool {b} differs outside band"
             exact = exact and np.array_equal(g, ref_keep)
         else:
             assert np.array_equal(g, ref_keep), (f"{prob.name}: pool {b} kept set differs "
                                                  f"({np.sum(g != ref_keep)} positions)")
     return exact
+
+
+def tie_band(m, k, rtol):
+    """Candidates of one pool (oracle masses m, -inf for non-finite) whose
+    membership in the top k is not fixed by the mass tolerance: those with
+    m_(k) - 2 tau <= m <= m_(k+1) + 2 tau (see the module docstring)."""
+    n = len(m)
+    if k == 0 or k == n:
+        return np.zeros(n, bool)
+    srt = np.sort(m)[::-1]
+    mk, mk1 = srt[k - 1], srt[k]
+    if not (np.isfinite(mk) and np.isfinite(mk1)):
+        return np.zeros(n, bool)
+    tau = max(rtol * abs(mk) / (1.0 - 2.0 * rtol), 1e-6)
+    return (m >= mk - 2 * tau) & (m <= mk1 + 2 * tau)
 
 
 def check_compaction_valid(prob, keep, comp, emb=None):

@@ -116,6 +116,120 @@ def test_mpmath_bruteforce_tiny(mask):
         assert abs(mass[c] - float(ref_mass[c])) <= 1e-12 * max(1.0, float(ref_mass[c]))
 
 
+# ---------------------------------------------------------------------------
+# The row-at-a-time LSE (``lse_rows``), the checker of the GPU LSE at sizes
+# where the full oracle is too slow: pinned to brute force, to the zero-key
+# closed form and to planted mistakes of its own, independently of
+# ``attention_stats``.
+# ---------------------------------------------------------------------------
+
+LSE_ROWS_LAYOUTS = {
+    # two requests, a text prefix, text between images and after them
+    "full": [(9, [(1, 1, 3), (5, 1, 2)]), (5, [(0, 2, 2)])],
+    "causal": [(9, [(1, 1, 3), (5, 1, 2)]), (5, [(0, 2, 2)])],
+    # every token inside an image; images of unequal sizes in two requests
+    "blockdiag": [(7, [(0, 1, 3), (3, 2, 2)]), (6, [(0, 2, 3)])],
+}
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "blockdiag"])
+def test_lse_rows_mpmath_bruteforce_gqa(mask):
+    """Every row of a two-request layout with GQA (6 query heads on 2 KV
+    heads, so a wrong head mapping reads the other KV head) against the
+    50-digit brute force, whose visibility comes from the mask's wording."""
+    rng = np.random.default_rng(12)
+    reqs = LSE_ROWS_LAYOUTS[mask]
+    T = sum(r[0] for r in reqs)
+    q = rng.standard_normal((T, 6, 4)) * 1.5
+    k = rng.standard_normal((T, 2, 4)) * 1.5
+    prob = handmade(reqs, q, k, mask)
+    got = oracle.lse_rows(prob, list(range(T)))
+    ref_lse, _ = mp_reference(prob)
+    for h in range(6):
+        for i in range(T):
+            assert ref_lse[h][i] is not None
+            assert abs(got[h, i] - float(ref_lse[h][i])) <= 1e-12 * max(1.0, abs(got[h, i])), (h, i)
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "blockdiag"])
+def test_lse_rows_zero_keys_count_visible(mask):
+    """Zero keys make every visible logit 0, so LSE_i = log(number of keys row
+    i sees): the request length (full), the position in the request plus one
+    (causal) or the image size (block-diagonal).  A wrong key range under any
+    mask changes the count."""
+    reqs = {"full": [(40, [(3, 4, 5)]), (23, [(2, 3, 3)]), (7, [])],
+            "causal": [(40, [(3, 4, 5)]), (23, [(2, 3, 3)]), (7, [])],
+            "blockdiag": [(20, [(0, 4, 5)]), (9, [(0, 3, 3)]), (30, [(0, 2, 3), (6, 4, 6)])]}[mask]
+    prob = make_problem("zero_k_" + mask, reqs, 4, 2, 64, "f32", mask, 1.0, 13, ratios=0.5)
+    prob.k = torch.zeros_like(prob.k)
+    T = prob.T
+    got = oracle.lse_rows(prob, list(range(T)))
+    want = np.empty(T)
+    for b in range(prob.B):
+        lo, hi = int(prob.cu_seqlens[b]), int(prob.cu_seqlens[b + 1])
+        for t in range(lo, hi):
+            want[t] = (hi - lo) if mask == "full" else (t - lo + 1)
+    if mask == "blockdiag":
+        for s in range(prob.S):
+            n = int(prob.img_hw[s, 0] * prob.img_hw[s, 1])
+            want[prob.img_start[s]:prob.img_start[s] + n] = n
+    np.testing.assert_allclose(got, np.broadcast_to(np.log(want), got.shape), rtol=0, atol=1e-13)
+
+
+def test_lse_rows_sampled_rows_and_repeated_heads():
+    """Sampled rows of a GQA problem equal the same rows of the problem with
+    its K heads repeated (MHA), and a row's value does not depend on which
+    other rows are asked for."""
+    prob = random_small(14, "causal", dtype="bf16", hq=8, hkv=2, d=64, n_req=3)
+    rows = [0, 5, prob.T // 2, prob.T - 1]
+    a = oracle.lse_rows(prob, rows)
+    mha = random_small(14, "causal", dtype="bf16", hq=8, hkv=2, d=64, n_req=3)
+    mha.k = prob.k.repeat_interleave(4, dim=1)
+    b = oracle.lse_rows(mha, rows)
+    np.testing.assert_array_equal(a, b)
+    c = oracle.lse_rows(prob, rows[::-1])[:, ::-1]
+    np.testing.assert_array_equal(a, c)
+
+
+def _lse_rows_variant(kind):
+    """A copy of the row-at-a-time LSE with one planted mistake."""
+    def f(prob, tokens, scale=None):
+        q64, k64 = O.to_f64(prob.q), O.to_f64(prob.k)
+        hq, hkv, d = q64.shape[1], k64.shape[1], q64.shape[2]
+        rep = hq // hkv
+        scale = O.problem_scale(prob, d) if scale is None else scale
+        segs = O.attention_segments(prob)
+        if kind == "blockdiag_as_request":
+            segs = [(int(prob.cu_seqlens[b]), int(prob.cu_seqlens[b + 1])) + s[2:]
+                    for b in range(prob.B) for s in segs[:1]]
+        out = np.full((hq, len(tokens)), np.nan)
+        for col, t in enumerate(tokens):
+            for lo, hi, *_ in segs:
+                if lo <= t < hi:
+                    kend = (t if kind == "causal_off_by_one" else t + 1) if prob.mask == "causal" else hi
+                    kend = max(kend, lo + 1)
+                    for h in range(hq):
+                        g = h % hkv if kind == "gqa_modulo" else h // rep
+                        z = scale * (k64[lo:kend, g, :] @ q64[t, h, :])
+                        m = z.max()
+                        out[h, col] = m + np.log(np.exp(z - m).sum())
+        return out
+    return f
+
+
+@pytest.mark.parametrize("kind", ["causal_off_by_one", "gqa_modulo", "blockdiag_as_request"])
+def test_lse_rows_planted_mistakes_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "lse_rows", _lse_rows_variant(kind))
+    caught = 0
+    for check in ([lambda m=m: test_lse_rows_mpmath_bruteforce_gqa(m) for m in ("full", "causal", "blockdiag")] +
+                  [lambda m=m: test_lse_rows_zero_keys_count_visible(m) for m in ("causal", "blockdiag")]):
+        try:
+            check()
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, kind
+
+
 def test_fp8_decoder_matches_format():
     """OCP E4M3: every byte code against torch's float8_e4m3fn widening, and
     the format's landmarks (largest finite 448, smallest normal 2^-6, smallest

@@ -228,30 +228,65 @@ def input_digest(prob):
 
 
 def test_varlen_supplied_lse_full_size(dev):
-    """Varlen batch with the LSE supplied (the oracle's, rounded to fp32):
-    sampled requests against live oracle masses, every pool and the
-    compaction checked for validity, plus the supplied-LSE shift identity."""
+    """Varlen batch with the LSE supplied (the oracle's, rounded to fp32, as a
+    FlashAttention forward would hand it over): every score of all eight
+    requests against the live oracle masses computed from that same fp32
+    LSE, every pool's kept set, and the compaction bit-exact when the kept
+    sets agree."""
     prob = make_config(5)
     announce(prob)
     workers = oracle.default_workers()
     lse64, _ = oracle.attention_stats(prob, workers=workers)
     lse32 = lse64.astype(np.float32)
     got = P.run_gpu(prob, dev, lse=lse32)
-    sizes = np.diff(prob.cu_seqlens)
-    sample = [int(b) for b in np.argsort(sizes)[:2]]
-    _, ref_mass = oracle.attention_stats(prob, lse_in=lse32, workers=workers, segments=sample)
-    bounds = oracle.pool_bounds(prob)
-    cands = np.concatenate([np.arange(*bounds[b]) for b in sample])
-    P.check_scores(prob, got["score"], ref_mass, cands=cands)
+    _, ref_mass = oracle.attention_stats(prob, lse_in=lse32, workers=workers)
+    P.check_scores(prob, got["score"], ref_mass)
     ref_keep, ref_k = oracle.topk(prob, oracle.scores(prob, ref_mass))
     assert np.array_equal(got["k"], ref_k)
-    P.check_keep(prob, got["keep"], ref_mass, ref_k, pools=sample)
+    exact = P.check_keep(prob, got["keep"], ref_mass, ref_k)
     P.check_compaction_valid(prob, got["keep"], got["compact"], prob.emb)
-    # Every pool: the GPU's kept set is a valid top-k of the GPU's scores.
-    for b, (lo, hi) in enumerate(bounds):
-        s, kp = got["score"][lo:hi], got["keep"][lo:hi].astype(bool)
-        if 0 < kp.sum() < hi - lo:
-            assert s[kp].min() >= s[~kp].max()
+    if exact:
+        P.check_compaction_exact(prob, got["compact"], oracle.compact(prob, ref_keep), prob.emb)
+    print(f"[check] {prob.B} pools, {prob.N} candidates compared; kept sets exact: {exact}", flush=True)
+
+
+# Logit offsets (natural log) of a planted large-norm key above the ordinary
+# logits.  The LSE kernel sums exp2(c1*s - m) against m = (largest logit of
+# the first key tile) + 32 in log2 units, and redoes a workgroup exactly (max
+# pass, then sum pass) when any row sum leaves [2^-100, 2^100], i.e. when a
+# later key's logit exceeds the first tile's largest by more than 132 log2
+# units = 91.5 nats.  50 nats stays on the one-pass path with terms up to
+# 2^40; 150 nats forces the exact path.
+@pytest.mark.parametrize("nats", [50.0, 150.0])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f16", 128)])
+def test_lse_large_logit_range_one_pass_and_exact_fallback(dev, nats, dtype, d):
+    """Q rows share a direction u; two keys, one at token 40 of the first
+    request (past the first 32-key tile, first row block) and one at token
+    300 of the second request (a later row block: 256 tokens per row block
+    at d = 64, 2 query heads per KV head), are set to alpha * u so that every
+    row after them sees a logit about `nats` above the others.  LSE, scores,
+    kept sets and compaction against the live oracle."""
+    reqs = [(420, [(8, 12, 16), (220, 10, 12)]), (520, [(30, 16, 16), (320, 12, 14)])]
+    prob = make_problem(f"large_logit_{int(nats)}nats_{dtype}_d{d}", reqs, 4, 2, d, dtype, "causal",
+                        0.5, 41, ratios=0.5, emb_dim=16)
+    rng = np.random.default_rng(42)
+    u = torch.from_numpy(rng.choice([-1.0, 1.0], size=d).astype(np.float32))
+    q = prob.q.float()
+    q = 0.5 * u + 0.5 * q  # shared direction plus noise of std 0.25
+    # alpha: scale * (0.5 u) . (alpha u) = alpha * 0.5 * d / sqrt(d) = nats.
+    alpha = nats / (0.5 * d ** 0.5)
+    k = prob.k.float()
+    t0 = int(prob.cu_seqlens[1])
+    for t in (40, t0 + 300):
+        k[t, :, :] = alpha * u
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    prob.q, prob.k = q.to(tdt), k.to(tdt)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    ref = oracle.run(prob, with_emb=False)
+    # The planted keys do sit far above the first key tile of the rows after them.
+    assert np.median(ref["lse"][:, 45:int(prob.cu_seqlens[1])]) > nats - 5
+    P.full_check(prob, got, ref, prob.emb)
 
 
 @pytest.mark.parametrize("cfg", [4, 5])
