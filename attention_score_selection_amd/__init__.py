@@ -6,10 +6,10 @@ call names.
 """
 from .binding import (EXPORTS, LIB_PATH, Layout, TselError, lib, select, tsel_attention_fwd,
                       tsel_budget_mass, tsel_budget_topk,
-                      tsel_colscore, tsel_compact, tsel_lse, tsel_mrope_positions,
-                      tsel_workspace_size)
+                      tsel_colscore, tsel_colscore_noalloc, tsel_compact, tsel_lse,
+                      tsel_mrope_positions, tsel_workspace_size)
 
 __all__ = ["EXPORTS", "LIB_PATH", "Layout", "TselError", "lib", "select", "tsel_attention_fwd",
            "tsel_budget_mass", "tsel_budget_topk",
-           "tsel_colscore", "tsel_compact", "tsel_lse", "tsel_mrope_positions",
-           "tsel_workspace_size"]
+           "tsel_colscore", "tsel_colscore_noalloc", "tsel_compact", "tsel_lse",
+           "tsel_mrope_positions", "tsel_workspace_size"]

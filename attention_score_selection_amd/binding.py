@@ -20,7 +20,7 @@ TSEL_OK, TSEL_EINVAL, TSEL_EUNSUPPORTED, TSEL_EWORKSPACE, TSEL_EHIP = 0, -1, -2,
 TSEL_F32, TSEL_F16, TSEL_BF16, TSEL_FP8_E4M3 = 0, 1, 2, 3
 MASKS = {"full": 0, "causal": 1, "blockdiag": 2}
 TSEL_OP_LSE, TSEL_OP_COLSCORE, TSEL_OP_TOPK, TSEL_OP_COMPACT, TSEL_OP_MROPE = 0, 1, 2, 3, 4
-EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_budget_topk", "tsel_compact", "tsel_mrope_positions",
+EXPORTS = ("tsel_lse", "tsel_colscore", "tsel_colscore_noalloc", "tsel_budget_topk", "tsel_compact", "tsel_mrope_positions",
            "tsel_attention_fwd", "tsel_budget_mass",
            "tsel_workspace_size", "tsel_last_error", "tsel_version")
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.tsel_colscore.restype = ctypes.c_int
         L.tsel_colscore.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P, _P, _P,
                                     ctypes.c_size_t, _P]
+        L.tsel_colscore_noalloc.restype = ctypes.c_int
+        L.tsel_colscore_noalloc.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P, _P, _P]
         L.tsel_budget_topk.restype = ctypes.c_int
         L.tsel_budget_topk.argtypes = [ctypes.POINTER(CLayout), _P, _P, _P, _P, _P]
         L.tsel_budget_mass.restype = ctypes.c_int
@@ -193,6 +195,19 @@ def tsel_colscore(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask: str, l
     _check(lib().tsel_colscore(ctypes.byref(attn), ctypes.byref(layout.c), _ptr(lse), _ptr(out),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(q.device)))
+    return out
+
+
+def tsel_colscore_noalloc(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask: str, lse: torch.Tensor,
+                          softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """tsel_colscore with the library's static device scratch (no workspace)."""
+    attn = make_attn(q, k, mask, softmax_scale)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [Hq, T] tensor")
+    if out is None:
+        out = torch.empty((layout.N,), dtype=torch.float32, device=q.device)
+    _check(lib().tsel_colscore_noalloc(ctypes.byref(attn), ctypes.byref(layout.c), _ptr(lse), _ptr(out),
+                                       _stream(q.device)))
     return out
 
 

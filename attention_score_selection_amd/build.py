@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libtsel.so")
-SOURCES = ["api.cpp", "attn.hip", "fwd.hip", "select.hip"]
+SOURCES = ["api.cpp", "attn.hip", "fwd.hip", "select.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 

@@ -450,8 +450,16 @@ int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, v
   return TSEL_OK;
 }
 
-int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
-                  float *score, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace tsel {
+
+// tsel_colscore and tsel_colscore_noalloc: validation and planning, then the
+// same kernels with the partials either in the caller's workspace or (noalloc)
+// in the library's static device scratch.
+static int colscore_call(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
+                         float *score, void *workspace, size_t workspace_bytes, bool noalloc,
+                         void *stream) {
   clear_error();
   int rc = check_layout(layout);
   if (rc == TSEL_OK) rc = check_attn(attn, layout);
@@ -462,6 +470,16 @@ int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const fl
   if (((uintptr_t)lse | (uintptr_t)score) & 3) return fail(TSEL_EINVAL, "lse/score must be 4-byte aligned");
   AttnPlan p;
   if ((rc = plan_colscore(attn, layout, &p)) != TSEL_OK) return rc;
+  if (noalloc) {
+    if (p.partial_bytes > kStaticScratchBytes)
+      return fail(TSEL_EWORKSPACE,
+                  "tsel_colscore_noalloc: this problem needs %zu bytes of column-score scratch, more than the "
+                  "library's static %zu bytes; call tsel_colscore with a workspace instead",
+                  p.partial_bytes, kStaticScratchBytes);
+    const hipError_t e = static_scratch(&workspace);
+    if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_colscore_noalloc: scratch address: %s", hipGetErrorString(e));
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (p.partial_bytes > 0 && (workspace == nullptr || workspace_bytes < p.partial_bytes))
     return fail(TSEL_EWORKSPACE, "tsel_colscore needs %zu workspace bytes (got %zu)", p.partial_bytes,
                 workspace_bytes);
@@ -475,6 +493,20 @@ int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const fl
       launch_colscore(p, a, a.order != kOrderPlain ? &perm : nullptr, score, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_colscore launch: %s", hipGetErrorString(e));
   return TSEL_OK;
+}
+
+}  // namespace tsel
+
+extern "C" {
+
+int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
+                  float *score, void *workspace, size_t workspace_bytes, void *stream) {
+  return colscore_call(attn, layout, lse, score, workspace, workspace_bytes, false, stream);
+}
+
+int tsel_colscore_noalloc(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
+                          float *score, void *stream) {
+  return colscore_call(attn, layout, lse, score, nullptr, 0, true, stream);
 }
 
 int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const double *keep_ratio_h,

@@ -160,6 +160,11 @@ hipError_t launch_mrope(const DevLayout &L, int *adj, const int *tok, const int 
 
 constexpr int kCompactBlock = 1024;
 
+// The static device scratch of tsel_colscore_noalloc (static_scratch.hip):
+// its size, and its address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void **out);
+
 // Streamed tiles are read through buffer resources whose range ends here;
 // offsets at or past it read as zero.
 constexpr int kBufferLimit = 0x7FFFFFF0;

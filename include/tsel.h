@@ -158,6 +158,20 @@ int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, v
 int tsel_colscore(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
                   float *score, void *workspace, size_t workspace_bytes, void *stream);
 
+/* tsel_colscore for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels, with the column-score partials in a
+ * static device buffer of the library (16 MiB, one per GPU, held until the
+ * process ends) instead of a caller workspace.  The call allocates and frees
+ * nothing.  Problems whose partials need more than 16 MiB
+ * (tsel_workspace_size(TSEL_OP_COLSCORE) > 16 MiB) return TSEL_EWORKSPACE
+ * before enqueuing anything.  Every call on one GPU shares that GPU's buffer:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * give wrong scores; calls ordered on one stream are safe.  Arguments, output
+ * and errors otherwise as tsel_colscore. */
+int tsel_colscore_noalloc(const tsel_attn_t *attn, const tsel_layout_t *layout, const float *lse,
+                          float *score, void *stream);
+
 /* Global budget per request (REDtech article, sections 3.1-3.2: all images of
  * a request compete in one pool; LiteVLM review, section 3.2 / section 5 table:
  * keep ratio r).  For pool b with N_b candidates,

@@ -185,6 +185,25 @@ def test_workspace_sizes_and_shortfall(lib):
     assert rc == B.TSEL_EWORKSPACE
 
 
+def test_colscore_noalloc_rejects_problems_over_its_static_scratch(lib):
+    """tsel_colscore_noalloc keeps its partials in a 16 MiB static device
+    buffer: a problem needing more is refused before any HIP call."""
+    # One 32768-token request, 30000 candidates (30 images of 25 x 40), 64/8 heads:
+    # 8 head blocks x 35 row chunks x 30000 candidates x 4 bytes = 33.6 MB.
+    starts = [100 + 1000 * i for i in range(30)]
+    lay = HostLayout([0, 32768], [0, 30], starts, [[25, 40]] * 30,
+                     [1000 * i for i in range(31)])
+    a = attn(hq=64, hkv=8, d=128)
+    need = lib.tsel_workspace_size(B.TSEL_OP_COLSCORE, ctypes.byref(a), ctypes.byref(lay.c))
+    assert need > 16 << 20
+    rc = lib.tsel_colscore_noalloc(ctypes.byref(a), ctypes.byref(lay.c), FAKE, FAKE, None)
+    assert rc == B.TSEL_EWORKSPACE
+    assert "16777216" in last_error(lib) and str(need) in last_error(lib)
+    # Validation errors come first, as in tsel_colscore.
+    assert lib.tsel_colscore_noalloc(ctypes.byref(attn(d=112)), ctypes.byref(lay.c), FAKE, FAKE,
+                                     None) == B.TSEL_EUNSUPPORTED
+
+
 def test_colscore_cuts_the_last_chunk_of_long_segments(lib):
     """Row chunks of 8192 query rows (512 tokens at 16 folded heads); a
     segment longer than one chunk, in a launch with at least 512 jobs, has
