@@ -38,7 +38,7 @@ class TselError(RuntimeError):
 
 class CLayout(ctypes.Structure):
     _fields_ = [("num_reqs", ctypes.c_int32), ("num_images", ctypes.c_int32),
-                ("total_tokens", ctypes.c_int32),
+                ("total_tokens", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
                 ("cu_seqlens", _P), ("cu_images", _P), ("img_start", _P), ("img_hw", _P),
                 ("cu_cands", _P),
                 ("cu_seqlens_h", _P), ("cu_images_h", _P), ("img_start_h", _P), ("img_hw_h", _P),
@@ -68,14 +68,14 @@ def lib() -> ctypes.CDLL:
         L.tsel_workspace_size.restype = ctypes.c_size_t
         L.tsel_workspace_size.argtypes = [ctypes.c_int, ctypes.POINTER(CAttn), ctypes.POINTER(CLayout)]
         L.tsel_lse.restype = ctypes.c_int
-        L.tsel_lse.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P, _P]
+        L.tsel_lse.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P, _P, ctypes.c_size_t, _P]
         L.tsel_colscore.restype = ctypes.c_int
         L.tsel_colscore.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P, _P, _P,
                                     ctypes.c_size_t, _P]
         L.tsel_colscore_noalloc.restype = ctypes.c_int
         L.tsel_colscore_noalloc.argtypes = [ctypes.POINTER(CAttn), ctypes.POINTER(CLayout), _P, _P, _P]
         L.tsel_budget_topk.restype = ctypes.c_int
-        L.tsel_budget_topk.argtypes = [ctypes.POINTER(CLayout), _P, _P, _P, _P, _P]
+        L.tsel_budget_topk.argtypes = [ctypes.POINTER(CLayout), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.tsel_budget_mass.restype = ctypes.c_int
         L.tsel_budget_mass.argtypes = [ctypes.POINTER(CLayout), _P, _P, _P, _P, _P, _P, _P]
         L.tsel_compact.restype = ctypes.c_int
@@ -129,6 +129,7 @@ class Layout:
         self.N = int(self.h["cu_cands"][-1])
         c = CLayout()
         c.num_reqs, c.num_images, c.total_tokens = self.B, self.S, self.T
+        c.max_seqlen = int(np.diff(self.h["cu_seqlens"]).max(initial=0))
         for name in self.h:
             setattr(c, name + "_h", self.h[name].ctypes.data if self.h[name].size else None)
             setattr(c, name, self.d[name].data_ptr() if (self.d and self.h[name].size) else None)
@@ -170,13 +171,24 @@ def tsel_workspace_size(op: int, layout: Layout, q=None, k=None, mask="causal",
     return int(n)
 
 
+def _workspace(need: int, workspace: Optional[torch.Tensor], device) -> torch.Tensor:
+    """The caller's workspace if it is large enough, else a new one."""
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=device)
+    return workspace
+
+
 def tsel_lse(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask: str,
-             softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Per-row softmax LSE, fp32 [Hq, T]."""
     attn = make_attn(q, k, mask, softmax_scale)
     if out is None:
         out = torch.empty((q.shape[1], layout.T), dtype=torch.float32, device=q.device)
-    _check(lib().tsel_lse(ctypes.byref(attn), ctypes.byref(layout.c), _ptr(out), _stream(q.device)))
+    need = tsel_workspace_size(TSEL_OP_LSE, layout, q, k, mask, softmax_scale)
+    ws = _workspace(need, workspace, q.device) if need > 0 else None
+    _check(lib().tsel_lse(ctypes.byref(attn), ctypes.byref(layout.c), _ptr(out), _ptr(ws),
+                          0 if ws is None else ws.numel() * ws.element_size(), _stream(q.device)))
     return out
 
 
@@ -190,8 +202,7 @@ def tsel_colscore(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask: str, l
     if out is None:
         out = torch.empty((layout.N,), dtype=torch.float32, device=q.device)
     need = tsel_workspace_size(TSEL_OP_COLSCORE, layout, q, k, mask, softmax_scale)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(need, workspace, q.device)
     _check(lib().tsel_colscore(ctypes.byref(attn), ctypes.byref(layout.c), _ptr(lse), _ptr(out),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(q.device)))
@@ -212,7 +223,7 @@ def tsel_colscore_noalloc(q: torch.Tensor, k: torch.Tensor, layout: Layout, mask
 
 
 def tsel_budget_topk(layout: Layout, score: torch.Tensor, keep_ratio: Sequence[float],
-                     out: Optional[torch.Tensor] = None):
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Keep flags (uint8 [N]) and k per pool (numpy int32 [B])."""
     ratios = np.ascontiguousarray(np.asarray(keep_ratio, np.float64).reshape(-1))
     if ratios.size != layout.B:
@@ -220,8 +231,11 @@ def tsel_budget_topk(layout: Layout, score: torch.Tensor, keep_ratio: Sequence[f
     k_h = np.zeros(layout.B, np.int32)
     if out is None:
         out = torch.empty((layout.N,), dtype=torch.uint8, device=score.device)
+    need = tsel_workspace_size(TSEL_OP_TOPK, layout)
+    ws = _workspace(need, workspace, score.device) if need > 0 else None
     _check(lib().tsel_budget_topk(ctypes.byref(layout.c), _ptr(score), ratios.ctypes.data,
-                                  k_h.ctypes.data, _ptr(out), _stream(score.device)))
+                                  k_h.ctypes.data, _ptr(out), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(score.device)))
     return out, k_h
 
 
@@ -265,8 +279,7 @@ def tsel_compact(layout: Layout, keep: torch.Tensor, k_per_pool, emb: Optional[t
         emb_ptr, emb_stride, row_bytes = emb.data_ptr(), emb.stride(0) * es, emb.shape[1] * es
         out_ptr, out_stride = o["emb"].data_ptr(), o["emb"].stride(0) * es
     need = tsel_workspace_size(TSEL_OP_COMPACT, layout)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    workspace = _workspace(need, workspace, dev)
     _check(lib().tsel_compact(ctypes.byref(layout.c), _ptr(keep), emb_ptr, emb_stride, row_bytes,
                               t_out, out_ptr, out_stride, _ptr(o["token_idx"]), _ptr(o["spatial"]),
                               _ptr(o["cu_seqlens"]), _ptr(o["img_counts"]), _ptr(workspace),

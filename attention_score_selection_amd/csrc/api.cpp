@@ -73,6 +73,12 @@ static int check_layout(const tsel_layout_t *l) {
     return fail(TSEL_EINVAL, "img_start/img_hw (host and device) are required when num_images > 0");
   const int32_t *cu = l->cu_seqlens_h, *ci = l->cu_images_h, *cc = l->cu_cands_h;
   if (cu[0] != 0 || cu[B] != T) return fail(TSEL_EINVAL, "cu_seqlens must run from 0 to total_tokens");
+  if (l->max_seqlen != 0) {
+    int32_t longest = 0;
+    for (int b = 0; b < B; ++b) longest = std::max(longest, cu[b + 1] - cu[b]);
+    if (l->max_seqlen != longest)
+      return fail(TSEL_EINVAL, "max_seqlen is %d but the longest request has %d tokens", l->max_seqlen, longest);
+  }
   if (ci[0] != 0 || ci[B] != S) return fail(TSEL_EINVAL, "cu_images must run from 0 to num_images");
   if (cc[0] != 0) return fail(TSEL_EINVAL, "cu_cands[0] must be 0");
   for (int b = 0; b < B; ++b) {
@@ -161,27 +167,76 @@ static void seg_sizes(const tsel_layout_t *l, int kind, int a, long long &n, lon
   }
 }
 
-// Row blocks of 4 waves x NG resident 32-row groups; fall back to one group
-// per wave when the grid would be small.
+// Row blocks of 4 waves x NG resident 32-row groups.  A grid of at least 512
+// jobs (two workgroups per CU) runs as it is.  A smaller one (a short causal
+// request, a few heads) takes one group per wave and splits every row
+// block's keys into ranges of KS keys whose partial log-sum-exps a merge pass
+// combines: the largest KS in 2048 .. 256 that gives 1024 jobs with keys
+// (measured on the 3214-token, 16-head layer: 47 us with 512-key splits,
+// 53-62 us with 256 or 1024, 63 us unsplit, 111 us unsplit with three groups
+// per wave).  The partials take Hq * T * (splits of the longest segment)
+// floats of workspace.
 int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
   if (int rc = check_offsets(a, l, p->F)) return rc;
-  const int ng_max = max_groups(a->dtype, a->head_dim);
-  for (int ng = ng_max;; ng = 1) {
-    p->NT = ng;
-    p->TB = 4 * ng * 32 / p->F;
-    long long R = 0;
+  const bool causal = a->mask == TSEL_MASK_CAUSAL;
+  // all: jobs launched; real: jobs that see at least one key.
+  auto count = [&](int ng, int KS, long long &all, long long &real, long long &nmax) {
+    const int TB = 4 * ng * 32 / p->F;
+    all = real = nmax = 0;
     for (int s = 0; s < p->nseg; ++s) {
       long long n, nc;
       seg_sizes(l, p->segkind, s, n, nc);
-      R += (n + p->TB - 1) / p->TB;
+      nmax = std::max(nmax, n);
+      const long long nrb = (n + TB - 1) / TB, nks = KS ? (n + KS - 1) / KS : 1;
+      all += nrb * nks;
+      if (KS && causal) {
+        for (long long rb = 0; rb < nrb; ++rb) real += (std::min((rb + 1) * TB, n) + KS - 1) / KS;
+      } else {
+        real += nrb * nks;
+      }
     }
-    p->jobs_per_hb = R;
-    p->total_jobs = R * p->nhb;
-    if (p->total_jobs >= 512 || ng == 1) break;
+    all *= p->nhb;
+    real *= p->nhb;
+  };
+  auto choose = [&](int ng, int KS) {
+    long long all, real, nmax;
+    count(ng, KS, all, real, nmax);
+    p->NT = ng;
+    p->TB = 4 * ng * 32 / p->F;
+    p->KS = KS;
+    p->ksmax = KS ? (int)((nmax + KS - 1) / KS) : 0;
+    p->total_jobs = all;
+    p->jobs_per_hb = all / p->nhb;
+  };
+  const int ng_max = max_groups(a->dtype, a->head_dim);
+  long long all, real, nmax;
+  count(ng_max, 0, all, real, nmax);
+  if (all >= 512) {
+    choose(ng_max, 0);
+  } else {
+    // One group per wave (short jobs, more waves resident to cover latency)
+    // and the largest split that gives 1024 jobs with keys; failing that, the
+    // split with the most such jobs (no split when none divides a segment).
+    const int splits[4] = {2048, 1024, 512, 256};
+    int pick = 0;
+    long long best = -1;
+    for (int KS : splits) {
+      count(1, KS, all, real, nmax);
+      if (real >= 1024) {
+        pick = KS;
+        break;
+      }
+      if (real > best) {
+        best = real;
+        pick = KS;
+      }
+    }
+    count(1, pick, all, real, nmax);
+    choose(1, nmax > pick ? pick : 0);
   }
   p->KB = p->RC = p->RCF = p->RCmax = 0;
-  p->partial_bytes = 0;
+  p->partial_bytes = p->KS ? (size_t)a->num_heads_q * l->total_tokens * p->ksmax * sizeof(float) : 0;
   if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
   return TSEL_OK;
 }
@@ -201,6 +256,7 @@ int plan_fwd(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   p->jobs_per_hb = R;
   p->total_jobs = R * p->nhb;
   p->KB = p->RC = p->RCF = p->RCmax = 0;
+  p->KS = p->ksmax = 0;
   p->partial_bytes = 0;
   if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");
   return TSEL_OK;
@@ -254,6 +310,7 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   // 2 and 8 measured between).
   if (p->RC == rc_full && maxn > rc_full) plan_jobs(rc_full, rc_full / 4);
   p->TB = 0;
+  p->KS = p->ksmax = 0;
   p->RCmax = 1;
   for (int s = 0; s < p->nseg; ++s) {
     long long n, nc;
@@ -347,7 +404,7 @@ static void set_order(AttnArgs &x, JobPerm &perm, const tsel_attn_t *a, const ts
                       const AttnPlan &p, bool keyblocks, int mode) {
   x.order = kOrderPlain;
   memset(perm.w, 0, sizeof(perm.w));
-  if (mode == kOrderPlain || p.nseg < 2 || p.jobs_per_hb > kOrderMaxJobs) return;
+  if (mode == kOrderPlain || p.nseg < 2 || p.jobs_per_hb > kOrderMaxJobs || p.KS > 0) return;
   std::vector<int> w;
   job_weights(a, l, p, keyblocks, w);
   if ((long long)w.size() != p.jobs_per_hb) return;
@@ -384,12 +441,42 @@ static AttnArgs attn_args(const tsel_attn_t *a, const tsel_layout_t *l, const At
   x.total_jobs = (int)p.total_jobs;
   x.order = kOrderPlain;
   x.TB = p.TB;
+  x.KS = p.KS;
+  x.ksmax = p.ksmax;
   x.N = l->cu_cands_h[l->num_images];
   x.RC = p.RC;
   x.RCF = p.RCF;
   x.RCmax = p.RCmax;
   x.KB = p.KB;
   return x;
+}
+
+// Pools of more than kTopkRegLimit candidates, in launches of up to
+// kTopkLargeChunk pools; the workspace holds one launch's state.
+static void topk_large_launches(const tsel_layout_t *l, std::vector<TopkLarge> *out, long long *max_blocks) {
+  *max_blocks = 0;
+  TopkLarge cur{};
+  auto flush = [&]() {
+    if (cur.np == 0) return;
+    *max_blocks = std::max(*max_blocks, (long long)cur.blk[cur.np]);
+    if (out) out->push_back(cur);
+    cur = TopkLarge{};
+  };
+  for (int b = 0; b < l->num_reqs; ++b) {
+    const long long nb = l->cu_cands_h[l->cu_images_h[b + 1]] - l->cu_cands_h[l->cu_images_h[b]];
+    if (nb <= kTopkRegLimit) continue;
+    cur.pool[cur.np] = b;
+    cur.blk[cur.np + 1] = cur.blk[cur.np] + (int)((nb + kTopkSplit - 1) / kTopkSplit);
+    ++cur.np;
+    if (cur.np == kTopkLargeChunk) flush();
+  }
+  flush();
+}
+
+static size_t topk_ws(const tsel_layout_t *l) {
+  long long mb;
+  topk_large_launches(l, nullptr, &mb);
+  return mb > 0 ? topk_large_ws_bytes(mb) : 0;
 }
 
 static size_t compact_ws(const tsel_layout_t *l) {
@@ -411,9 +498,12 @@ size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t 
   clear_error();
   if (check_layout(layout) != TSEL_OK) return (size_t)-1;
   switch (op) {
-    case TSEL_OP_LSE:
+    case TSEL_OP_LSE: {
       if (check_attn(attn, layout) != TSEL_OK) return (size_t)-1;
-      return 0;
+      AttnPlan p;
+      if (plan_lse(attn, layout, &p) != TSEL_OK) return (size_t)-1;
+      return p.partial_bytes;
+    }
     case TSEL_OP_COLSCORE: {
       if (check_attn(attn, layout) != TSEL_OK) return (size_t)-1;
       AttnPlan p;
@@ -421,7 +511,7 @@ size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t 
       return p.partial_bytes;
     }
     case TSEL_OP_TOPK:
-      return 0;
+      return topk_ws(layout);
     case TSEL_OP_COMPACT:
       return compact_ws(layout);
     case TSEL_OP_MROPE:
@@ -432,7 +522,8 @@ size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t 
   }
 }
 
-int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, void *stream) {
+int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, void *workspace,
+             size_t workspace_bytes, void *stream) {
   clear_error();
   int rc = check_layout(layout);
   if (rc == TSEL_OK) rc = check_attn(attn, layout);
@@ -441,10 +532,14 @@ int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, v
   if ((uintptr_t)lse & 3) return fail(TSEL_EINVAL, "lse must be 4-byte aligned");
   AttnPlan p;
   if ((rc = plan_lse(attn, layout, &p)) != TSEL_OK) return rc;
+  if (p.partial_bytes > 0 && (workspace == nullptr || workspace_bytes < p.partial_bytes))
+    return fail(TSEL_EWORKSPACE, "tsel_lse needs %zu workspace bytes (got %zu)", p.partial_bytes, workspace_bytes);
+  if ((uintptr_t)workspace & 3) return fail(TSEL_EINVAL, "workspace must be 4-byte aligned");
   AttnArgs a = attn_args(attn, layout, p);
   JobPerm perm;
   set_order(a, perm, attn, layout, p, false, kOrderSorted);
   a.lse_out = lse;
+  a.lse_part = reinterpret_cast<float *>(workspace);
   const hipError_t e = launch_lse(p, a, a.order != kOrderPlain ? &perm : nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_lse launch: %s", hipGetErrorString(e));
   return TSEL_OK;
@@ -510,7 +605,7 @@ int tsel_colscore_noalloc(const tsel_attn_t *attn, const tsel_layout_t *layout, 
 }
 
 int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const double *keep_ratio_h,
-                     int32_t *k_h, uint8_t *keep, void *stream) {
+                     int32_t *k_h, uint8_t *keep, void *workspace, size_t workspace_bytes, void *stream) {
   clear_error();
   int rc = check_layout(layout);
   if (rc != TSEL_OK) return rc;
@@ -528,6 +623,13 @@ int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const doub
     k_h[b] = (int32_t)std::min(nb, std::max(0LL, k));
   }
   if (N == 0) return TSEL_OK;
+  std::vector<TopkLarge> large;
+  long long max_blocks;
+  topk_large_launches(layout, &large, &max_blocks);
+  const size_t need = max_blocks > 0 ? topk_large_ws_bytes(max_blocks) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(TSEL_EWORKSPACE, "tsel_budget_topk needs %zu workspace bytes (got %zu)", need, workspace_bytes);
+  if ((uintptr_t)workspace & 3) return fail(TSEL_EINVAL, "workspace must be 4-byte aligned");
   const DevLayout L = dev_layout(layout);
   for (int b0 = 0; b0 < B; b0 += 256) {
     TopkChunk ch;
@@ -535,6 +637,13 @@ int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const doub
     const int np = std::min(256, B - b0);
     for (int i = 0; i < 256; ++i) ch.k[i] = (i < np) ? k_h[b0 + i] : 0;
     const hipError_t e = launch_topk(L, score, ch, np, keep, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_budget_topk launch: %s", hipGetErrorString(e));
+  }
+  int *ws = reinterpret_cast<int *>(workspace);
+  const TopkLargeWs lw{ws, ws + kTopkLargeChunk * 4, ws + kTopkLargeChunk * 4 + kTopkLargeChunk * 256};
+  for (TopkLarge &tl : large) {
+    for (int i = 0; i < tl.np; ++i) tl.k[i] = k_h[tl.pool[i]];
+    const hipError_t e = launch_topk_large(L, score, tl, lw, keep, (hipStream_t)stream);
     if (e != hipSuccess) return fail(TSEL_EHIP, "tsel_budget_topk launch: %s", hipGetErrorString(e));
   }
   return TSEL_OK;

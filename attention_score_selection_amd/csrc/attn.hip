@@ -128,11 +128,15 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
-  const int TB = a.TB;
+  const int TB = a.TB, KS = a.KS;
+  // Jobs of a segment of n tokens: its row blocks, each split into ceil(n/KS)
+  // key ranges of KS keys when KS > 0 (the splits past a causal row block's
+  // last key are empty jobs).
   auto count = [&](int s) {
     int lo, hi;
     seg_tokens(a.L, a.segkind, s, lo, hi);
-    return (hi - lo + TB - 1) / TB;
+    const int nrb = (hi - lo + TB - 1) / TB;
+    return KS ? nrb * ((hi - lo + KS - 1) / KS) : nrb;
   };
   int hb, rj;
   job_of<ORD>(a, pa, job, hb, rj);
@@ -145,8 +149,10 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
   // registers (tile addresses built from them then stay scalar too).
   seg_lo = uni(seg_lo);
   seg_hi = uni(seg_hi);
+  const int nks = KS ? (seg_hi - seg_lo + KS - 1) / KS : 1;
   const int nrb = (seg_hi - seg_lo + TB - 1) / TB;
-  const int rb = a.causal ? nrb - 1 - local : local;  // causal: heaviest row blocks first
+  const int rbl = local / nks, ks = local % nks;
+  const int rb = a.causal ? nrb - 1 - rbl : rbl;  // causal: heaviest row blocks first
   const int tok_lo = seg_lo + rb * TB;
   const int tok_hi = min(tok_lo + TB, seg_hi);
 
@@ -156,8 +162,11 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
   const int wtok_max = wtok0 + NG * kRows / F - 1;
   const int h0 = hb * F;
   const int g = h0 / a.hg;
-  const int key_lo = seg_lo;
-  const int key_hi = a.causal ? tok_hi : seg_hi;
+  // Keys of this job: the row block's whole range, or its ks-th split.
+  const int key_lo = seg_lo + ks * KS;
+  const int key_end = a.causal ? tok_hi : seg_hi;
+  const int key_hi = KS ? min(key_end, key_lo + KS) : key_end;
+  if (key_lo >= key_hi) return;  // a causal row block before this split
   const int ntiles = (key_hi - key_lo + kRows - 1) / kRows;
 
   // Resident queries: row q of this wave is (token wtok0 + q / F, head h0 + q % F).
@@ -173,9 +182,10 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
   for (int n = 0; n < NG; ++n) qtok[n] = wtok0 + (n * kRows + (lane & 31)) / F;
   wait_vmem();
 
-  // Offset m: max logit of the first key tile (which every row sees) plus 32
-  // (log2 units); the sum pass then cannot overflow unless a later logit
-  // exceeds it by ~100, which the check below catches.
+  // Offset m: max logit of the first key tile (which every row sees, except,
+  // in a later key split of a causal row block, the rows before the split)
+  // plus 32 (log2 units); the sum pass then cannot overflow unless a later
+  // logit exceeds it by ~100, which the check below catches.
   float m[NG], acc[NG];
 #pragma unroll
   for (int n = 0; n < NG; ++n) m[n] = 0.f;
@@ -189,7 +199,8 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
     tot[n] = acc[n] + __shfl_xor(acc[n], 32, 64);
-    if (qtok[n] < tok_hi) ok = ok && (tot[n] <= 0x1p100f) && (tot[n] >= 0x1p-100f);  // false for NaN
+    const bool sees = qtok[n] < tok_hi && !(a.causal && qtok[n] < key_lo);
+    if (sees) ok = ok && (tot[n] <= 0x1p100f) && (tot[n] >= 0x1p-100f);  // false for NaN
   }
   if (!ok) s_bad = 1;
   __syncthreads();
@@ -209,11 +220,47 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
       const int q = n * kRows + lane;
       const int t = wtok0 + q / F;
       if (t < tok_hi) {
-        const float lse2 = m[n] + __log2f(tot[n]);
-        a.lse_out[(long long)(h0 + q % F) * a.L.T + t] = lse2 * 0.69314718055994530942f;
+        const float lse2 = (a.causal && t < key_lo) ? kNegInf : m[n] + __log2f(tot[n]);
+        const long long row = (long long)(h0 + q % F) * a.L.T + t;
+        if (KS) a.lse_part[row * a.ksmax + ks] = lse2;
+        else a.lse_out[row] = lse2 * 0.69314718055994530942f;
       }
     }
   }
+}
+
+// Key-split LSE: combine a row's per-split log2-sum-exp values l_s into
+// LSE = ln 2 * (M + log2 sum_s 2^(l_s - M)), M = max_s l_s, splits in order.
+// A row sees splits 0 .. (causal: the split holding its own token; else the
+// last).  A NaN partial makes the row's LSE NaN.
+__global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
+  const long long T = a.L.T;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)a.hq * T) return;
+  const int h = (int)(idx / T), t = (int)(idx % T);
+  const DevLayout &L = a.L;
+  int lo, hi;
+  if (a.segkind == SEG_REQ) {
+    const int b = upper_index(L.cu_seqlens, 0, L.B, t);
+    lo = L.cu_seqlens[b];
+    hi = L.cu_seqlens[b + 1];
+  } else {
+    const int s = upper_index(L.img_start, 0, L.S, t);
+    lo = L.img_start[s];
+    hi = lo + L.img_hw[2 * s] * L.img_hw[2 * s + 1];
+  }
+  const int last = a.causal ? (t - lo) / a.KS : (hi - lo - 1) / a.KS;
+  const float *p = a.lse_part + idx * a.ksmax;
+  float M = kNegInf;
+  bool nan = false;
+  for (int ks = 0; ks <= last; ++ks) {
+    const float v = p[ks];
+    nan = nan || (v != v);
+    M = fmaxf(M, v);
+  }
+  float sum = 0.f;
+  for (int ks = 0; ks <= last; ++ks) sum += fast_exp2(p[ks] - M);
+  a.lse_out[idx] = nan ? __builtin_nanf("") : (M + __log2f(sum)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------------------
@@ -534,12 +581,17 @@ hipError_t col_d(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipS
 
 hipError_t launch_lse(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   if (p.total_jobs == 0) return hipSuccess;
+  hipError_t e;
   switch (p.dtype) {
-    case TSEL_F32: return lse_d<TSEL_F32>(p, a, perm, s);
-    case TSEL_F16: return lse_d<TSEL_F16>(p, a, perm, s);
-    case TSEL_FP8_E4M3: return lse_d<TSEL_FP8_E4M3>(p, a, perm, s);
-    default: return lse_d<TSEL_BF16>(p, a, perm, s);
+    case TSEL_F32: e = lse_d<TSEL_F32>(p, a, perm, s); break;
+    case TSEL_F16: e = lse_d<TSEL_F16>(p, a, perm, s); break;
+    case TSEL_FP8_E4M3: e = lse_d<TSEL_FP8_E4M3>(p, a, perm, s); break;
+    default: e = lse_d<TSEL_BF16>(p, a, perm, s); break;
   }
+  if (e != hipSuccess || a.KS == 0) return e;
+  const long long rows = (long long)a.hq * a.L.T;
+  hipLaunchKernelGGL(lse_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_colscore(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, float *score,

@@ -52,6 +52,9 @@ struct AttnArgs {
   // LSE kernel
   float *lse_out;
   int TB;                // tokens per row block
+  int KS;                // keys per key split (0: every job sees its row block's whole key range)
+  int ksmax;             // splits of the longest segment (stride of lse_part)
+  float *lse_part;       // [Hq][T][ksmax] per-split log2-sum-exp (workspace), when KS > 0
   // column-score kernel
   const float *lse_in;
   float *partial;        // [nhb][RCmax][N]
@@ -72,6 +75,7 @@ struct FwdArgs {
 struct AttnPlan {
   int dtype, D, NT;
   int F, nhb, TB, KB, RC, RCF, RCmax;
+  int KS, ksmax;         // LSE key split (0: none) and the splits of the longest segment
   int nseg, segkind;
   long long jobs_per_hb, total_jobs;
   size_t partial_bytes;
@@ -128,6 +132,30 @@ struct TopkChunk {
 };
 hipError_t launch_topk(const DevLayout &L, const float *score, const TopkChunk &ks, int npools,
                        uint8_t *keep, hipStream_t s);
+
+// Pools larger than one top-k workgroup holds in registers are spread over
+// blocks of kTopkSplit candidates each (64 such pools a launch).  Workspace
+// (ints): per pool a state record and a 256-bin histogram, then one tie count
+// per block.
+constexpr int kTopkRegLimit = 32768;
+constexpr int kTopkSplit = 16384;
+constexpr int kTopkLargeChunk = 64;
+struct TopkLarge {
+  int np;                       // large pools in this launch
+  int pool[kTopkLargeChunk];    // their pool indices
+  int k[kTopkLargeChunk];       // k of each
+  int blk[kTopkLargeChunk + 1]; // first block of each; blk[np] = blocks of the launch
+};
+struct TopkLargeWs {
+  int *state;  // [kTopkLargeChunk][4]: tau prefix, keys still to keep at tau, keys equal to tau, blocks done
+  int *hist;   // [kTopkLargeChunk][256]
+  int *blkeq;  // [blocks]: keys equal to tau per block
+};
+inline size_t topk_large_ws_bytes(long long max_blocks) {
+  return (size_t)(kTopkLargeChunk * 4 + kTopkLargeChunk * 256 + max_blocks) * sizeof(int);
+}
+hipError_t launch_topk_large(const DevLayout &L, const float *score, const TopkLarge &tl, const TopkLargeWs &ws,
+                             uint8_t *keep, hipStream_t s);
 
 // Input-dependent budget: per-pool target fraction and k bounds (64 pools a launch).
 constexpr int kMassChunk = 64;

@@ -250,7 +250,150 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(DevLayout L, const f
   const int b = ks.b0 + blockIdx.x;
   const int lo = L.cu_cands[L.cu_images[b]];
   const int hi = L.cu_cands[L.cu_images[b + 1]];
+  if (hi - lo > kTopkRegLimit) return;  // spread over many blocks (topk_large_*)
   topk_pool(score + lo, hi - lo, ks.k[blockIdx.x], keep + lo, hist, sh, eqbuf, s_digit, s_above);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k of pools larger than kTopkRegLimit candidates, spread over blocks of
+// kTopkSplit candidates: four launches of the MSB-first radix descent (each
+// block adds its chunk's digit histogram to the pool's with integer atomics;
+// the last block of the pool to finish, found with an atomic counter after a
+// fence, picks the digit and clears the histogram for the next pass), then a
+// count of the keys equal to tau per block, then the flags (keys equal to tau
+// ranked by index across the pool's blocks in block order).
+// ---------------------------------------------------------------------------
+
+// The large pool slot and chunk of block `bid`.
+__device__ __forceinline__ int large_slot(const TopkLarge &tl, int bid) {
+  int i = 0;
+  while (i + 1 < tl.np && tl.blk[i + 1] <= bid) ++i;
+  return i;
+}
+
+__device__ __forceinline__ void large_pool_range(const DevLayout &L, const TopkLarge &tl, int i, int &lo, int &n) {
+  const int b = tl.pool[i];
+  lo = L.cu_cands[L.cu_images[b]];
+  n = L.cu_cands[L.cu_images[b + 1]] - lo;
+}
+
+__global__ __launch_bounds__(256) void topk_large_init(TopkLarge tl, TopkLargeWs ws) {
+  const int i = blockIdx.x;
+  ws.hist[256 * i + threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    ws.state[4 * i + 0] = 0;         // tau prefix
+    ws.state[4 * i + 1] = tl.k[i];   // keys still to keep among those matching the prefix
+    ws.state[4 * i + 2] = -1;        // keys equal to tau (after the last pass)
+    ws.state[4 * i + 3] = 0;         // blocks of this pass done
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_large_pass(DevLayout L, const float *score, TopkLarge tl,
+                                                               TopkLargeWs ws, int pass) {
+  __shared__ int hist[256];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int i = large_slot(tl, blockIdx.x);
+  int lo, n;
+  large_pool_range(L, tl, i, lo, n);
+  const int k = tl.k[i];
+  if (k <= 0 || k >= n) return;
+  const int c0 = (blockIdx.x - tl.blk[i]) * kTopkSplit, c1 = min(c0 + kTopkSplit, n);
+  const int shift = 24 - 8 * pass;
+  const uint32_t pmask = pass == 0 ? 0u : 0xffffffffu << (shift + 8);
+  const uint32_t prefix = (uint32_t)ws.state[4 * i + 0];
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  for (int c = c0 + tid; c < c1; c += kTopkThreads) {
+    const uint32_t u = score_key(score[lo + c]);
+    if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+  }
+  __syncthreads();
+  int *H = ws.hist + 256 * i;
+  if (tid < 256 && hist[tid] != 0) atomicAdd(&H[tid], hist[tid]);
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int nblk = tl.blk[i + 1] - tl.blk[i];
+    s_last = atomicAdd(&ws.state[4 * i + 3], 1) == nblk - 1;
+  }
+  __syncthreads();
+  if (!s_last || tid >= 64) return;
+  // The pool's last block: walk the digits from 255 down (lane l holds
+  // 255-4l .. 252-4l), reading the counts at the device level.
+  __threadfence();
+  const int kr = ws.state[4 * i + 1];
+  int c[4], csum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = __hip_atomic_load(&H[255 - 4 * lane - j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    csum += c[j];
+  }
+  int cb = wave_incl_scan(csum) - csum;  // keys with a larger digit
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (cb < kr && cb + c[j] >= kr) {
+      ws.state[4 * i + 0] = (int)(prefix | ((uint32_t)(255 - 4 * lane - j) << shift));
+      ws.state[4 * i + 1] = kr - cb;
+      ws.state[4 * i + 2] = c[j];
+    }
+    cb += c[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) H[4 * lane + j] = 0;
+  if (lane == 0) ws.state[4 * i + 3] = 0;
+}
+
+// Keys equal to tau per block, when not all of them are kept.
+__global__ __launch_bounds__(kTopkThreads) void topk_large_count(DevLayout L, const float *score, TopkLarge tl,
+                                                                TopkLargeWs ws) {
+  __shared__ int sh[17];
+  const int tid = threadIdx.x;
+  const int i = large_slot(tl, blockIdx.x);
+  int lo, n;
+  large_pool_range(L, tl, i, lo, n);
+  const int k = tl.k[i];
+  if (k <= 0 || k >= n || ws.state[4 * i + 2] == ws.state[4 * i + 1]) return;
+  const uint32_t tau = (uint32_t)ws.state[4 * i + 0];
+  const int c0 = (blockIdx.x - tl.blk[i]) * kTopkSplit, c1 = min(c0 + kTopkSplit, n);
+  int cnt = 0;
+  for (int c = c0 + tid; c < c1; c += kTopkThreads) cnt += score_key(score[lo + c]) == tau ? 1 : 0;
+  int tot;
+  block_excl_scan(cnt, sh, tot);
+  if (tid == 0) ws.blkeq[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_large_flags(DevLayout L, const float *score, TopkLarge tl,
+                                                                TopkLargeWs ws, uint8_t *keep) {
+  __shared__ int sh[17];
+  const int tid = threadIdx.x;
+  const int i = large_slot(tl, blockIdx.x);
+  int lo, n;
+  large_pool_range(L, tl, i, lo, n);
+  const int k = tl.k[i];
+  const int c0 = (blockIdx.x - tl.blk[i]) * kTopkSplit, c1 = min(c0 + kTopkSplit, n);
+  if (k <= 0 || k >= n) {
+    for (int c = c0 + tid; c < c1; c += kTopkThreads) keep[lo + c] = k >= n ? 1 : 0;
+    return;
+  }
+  const uint32_t tau = (uint32_t)ws.state[4 * i + 0];
+  const int kr = ws.state[4 * i + 1], neq = ws.state[4 * i + 2];
+  if (neq == kr) {
+    for (int c = c0 + tid; c < c1; c += kTopkThreads) keep[lo + c] = score_key(score[lo + c]) >= tau ? 1 : 0;
+    return;
+  }
+  // Keys equal to tau before this block, in block order.
+  int seen = 0;
+  for (int b = tl.blk[i]; b < (int)blockIdx.x; ++b) seen += ws.blkeq[b];
+  for (int base = c0; base < c1; base += kTopkThreads) {
+    const int c = base + tid;
+    const uint32_t u = c < c1 ? score_key(score[lo + c]) : 0u;
+    const int eq = (c < c1 && u == tau) ? 1 : 0;
+    int tot;
+    const int rank = block_excl_scan(eq, sh, tot) + seen;
+    if (c < c1) keep[lo + c] = (u > tau || (eq && rank < kr)) ? 1 : 0;
+    seen += tot;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -674,6 +817,18 @@ hipError_t launch_topk(const DevLayout &L, const float *score, const TopkChunk &
                        uint8_t *keep, hipStream_t s) {
   if (npools <= 0) return hipSuccess;
   hipLaunchKernelGGL(topk_kernel, dim3(npools), dim3(kTopkThreads), 0, s, L, score, ks, keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_large(const DevLayout &L, const float *score, const TopkLarge &tl, const TopkLargeWs &ws,
+                             uint8_t *keep, hipStream_t s) {
+  if (tl.np <= 0) return hipSuccess;
+  const int nblk = tl.blk[tl.np];
+  hipLaunchKernelGGL(topk_large_init, dim3(tl.np), dim3(256), 0, s, tl, ws);
+  for (int pass = 0; pass < 4; ++pass)
+    hipLaunchKernelGGL(topk_large_pass, dim3(nblk), dim3(kTopkThreads), 0, s, L, score, tl, ws, pass);
+  hipLaunchKernelGGL(topk_large_count, dim3(nblk), dim3(kTopkThreads), 0, s, L, score, tl, ws);
+  hipLaunchKernelGGL(topk_large_flags, dim3(nblk), dim3(kTopkThreads), 0, s, L, score, tl, ws, keep);
   return hipGetLastError();
 }
 

@@ -269,6 +269,9 @@ def main():
     ws_col = torch.empty((max(16, tsel.tsel_workspace_size(1, lay, q, k, prob.mask, scale)),),
                          dtype=torch.uint8, device=dev)
     ws_cmp = torch.empty((tsel.tsel_workspace_size(3, lay),), dtype=torch.uint8, device=dev)
+    ws_lse = torch.empty((max(16, tsel.tsel_workspace_size(0, lay, q, k, prob.mask, scale)),),
+                         dtype=torch.uint8, device=dev)
+    ws_topk = torch.empty((max(16, tsel.tsel_workspace_size(2, lay)),), dtype=torch.uint8, device=dev)
     _, ks = tsel.tsel_budget_topk(
         lay, tsel.tsel_colscore(q, k, lay, prob.mask, tsel.tsel_lse(q, k, lay, prob.mask, scale), scale),
         ratios)
@@ -281,16 +284,16 @@ def main():
 
     # A workload with a supplied LSE (the reuse path) takes it as an input: it
     # is computed once here, outside the timed step.
-    tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse)
+    tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse, workspace=ws_lse)
 
     def step(ev=None):
         if ev: ev[0].record(stream)
         if not prob.lse_supplied:
-            tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse)
+            tsel.tsel_lse(q, k, lay, prob.mask, scale, out=lse, workspace=ws_lse)
         if ev: ev[1].record(stream)
         tsel.tsel_colscore(q, k, lay, prob.mask, lse, scale, out=score, workspace=ws_col)
         if ev: ev[2].record(stream)
-        tsel.tsel_budget_topk(lay, score, ratios, out=keep)
+        tsel.tsel_budget_topk(lay, score, ratios, out=keep, workspace=ws_topk)
         if ev: ev[3].record(stream)
         tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
         if ev: ev[4].record(stream)

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TSEL_VERSION 3
+#define TSEL_VERSION 4
 
 #define TSEL_OK 0
 #define TSEL_EINVAL (-1)      /* bad pointer, size, offset, ratio or layout        */
@@ -93,6 +93,10 @@ typedef struct {
   int32_t num_reqs;               /* B >= 1                                         */
   int32_t num_images;             /* S >= 0                                         */
   int32_t total_tokens;           /* T = cu_seqlens[B]                              */
+  int32_t max_seqlen;             /* longest request, max_b (cu_seqlens[b+1] -
+                                     cu_seqlens[b]); checked against the host mirror
+                                     when nonzero (TSEL_EINVAL if it differs);
+                                     0 = not given                                  */
   const int32_t *cu_seqlens;      /* [B+1] device                                   */
   const int32_t *cu_images;       /* [B+1] device                                   */
   const int32_t *img_start;       /* [S]   device                                   */
@@ -143,8 +147,13 @@ size_t tsel_workspace_size(int op, const tsel_attn_t *attn, const tsel_layout_t 
  * section 3.2):  lse[h*T + i] = log sum_{j visible(i)} exp(scale * q_{i,h} . k_{j,g(h)}).
  * Output: lse, fp32 [Hq, T] contiguous, every entry written.  Arithmetic:
  * MFMA products in fp32, exp2/log2 in fp32.  Non-finite inputs give a
- * non-finite LSE for the rows that see them.  No workspace. */
-int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, void *stream);
+ * non-finite LSE for the rows that see them.
+ * Workspace: tsel_workspace_size(TSEL_OP_LSE) bytes, 4-byte aligned.  It is 0
+ * for grids that fill the GPU; a small grid (a short causal request, few
+ * heads) splits each row's keys into ranges whose partial log-sum-exps the
+ * workspace holds until a merge pass combines them in a fixed order. */
+int tsel_lse(const tsel_attn_t *attn, const tsel_layout_t *layout, float *lse, void *workspace,
+             size_t workspace_bytes, void *stream);
 
 /* Importance score of every candidate (LiteVLM review, formula section: the
  * attention a vision token receives; REDtech article, section 3.2: the
@@ -179,9 +188,12 @@ int tsel_colscore_noalloc(const tsel_attn_t *attn, const tsel_layout_t *layout, 
  * and the k_b candidates with the largest scores are kept; equal scores go to
  * the lower candidate index; NaN and +-inf scores rank as -inf.
  * keep_ratio_h: host [B]; NaN is TSEL_EINVAL.  k_h: host [B], written
- * synchronously.  keep: device uint8 [N], 1 = kept.  No workspace. */
+ * synchronously.  keep: device uint8 [N], 1 = kept.
+ * Workspace: tsel_workspace_size(TSEL_OP_TOPK) bytes, 4-byte aligned (0 when
+ * every pool fits one workgroup's registers). */
 int tsel_budget_topk(const tsel_layout_t *layout, const float *score, const double *keep_ratio_h,
-                     int32_t *k_h, uint8_t *keep, void *stream);
+                     int32_t *k_h, uint8_t *keep, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /* Input-dependent budget (the REDtech article, section 6.2, names choosing
  * the compression rate from the input as the next step and gives no rule;

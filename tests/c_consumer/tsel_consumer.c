@@ -82,12 +82,19 @@ static int check(void) {
   a.k_stride_tok = 2 * 112;
   a.k_stride_head = 112;
   a.mask = TSEL_MASK_CAUSAL;
-  if (tsel_lse(&a, &lay, (float *)(uintptr_t)4096, NULL) != TSEL_EUNSUPPORTED) return fail("head_dim");
+  if (tsel_lse(&a, &lay, (float *)(uintptr_t)4096, NULL, 0, NULL) != TSEL_EUNSUPPORTED) return fail("head_dim");
   if (strstr(tsel_last_error(), "head_dim") == NULL) return fail("head_dim message");
-  if (tsel_lse(NULL, &lay, NULL, NULL) != TSEL_EINVAL) return fail("null attn");
+  if (tsel_lse(NULL, &lay, NULL, NULL, 0, NULL) != TSEL_EINVAL) return fail("null attn");
   ratios[1] = NAN;
-  if (tsel_budget_topk(&lay, (const float *)fake, ratios, k_h, (uint8_t *)(uintptr_t)4096, NULL) != TSEL_EINVAL)
+  if (tsel_budget_topk(&lay, (const float *)fake, ratios, k_h, (uint8_t *)(uintptr_t)4096, NULL, 0, NULL) !=
+      TSEL_EINVAL)
     return fail("NaN ratio");
+  ratios[1] = 0.5;
+  lay.max_seqlen = 18; /* the longest request has 19 tokens */
+  if (tsel_budget_topk(&lay, (const float *)fake, ratios, k_h, (uint8_t *)(uintptr_t)4096, NULL, 0, NULL) !=
+      TSEL_EINVAL)
+    return fail("max_seqlen");
+  lay.max_seqlen = 19;
   if (tsel_workspace_size(TSEL_OP_COMPACT, NULL, &lay) == (size_t)-1) return fail("compact workspace size");
   lay.cu_seqlens_h = NULL;
   if (tsel_workspace_size(TSEL_OP_COMPACT, NULL, &lay) != (size_t)-1) return fail("missing host mirror");
@@ -123,7 +130,7 @@ static int run(const char *in_path, const char *out_path) {
   FILE *f = fopen(in_path, "rb");
   int32_t hdr[10];
   int32_t T, B, S, hq, hkv, d, dtype, mask, row_bytes, N, b, t_out;
-  size_t es, ws_bytes, ws_col, ws_cmp, ws_rope;
+  size_t es, ws_bytes, ws_lse, ws_col, ws_topk, ws_cmp, ws_rope;
   int32_t *cu_seqlens, *cu_images, *img_start, *img_hw, *cu_cands, *k_h;
   double *ratios;
   void *q_h, *k_hbuf, *emb_h;
@@ -158,6 +165,8 @@ static int run(const char *in_path, const char *out_path) {
   lay.num_reqs = B;
   lay.num_images = S;
   lay.total_tokens = T;
+  for (b = 0; b < B; ++b)
+    if (cu_seqlens[b + 1] - cu_seqlens[b] > lay.max_seqlen) lay.max_seqlen = cu_seqlens[b + 1] - cu_seqlens[b];
   lay.cu_seqlens = to_device(cu_seqlens, sizeof(int32_t) * (B + 1));
   lay.cu_images = to_device(cu_images, sizeof(int32_t) * (B + 1));
   lay.img_start = to_device(img_start, sizeof(int32_t) * S);
@@ -186,22 +195,29 @@ static int run(const char *in_path, const char *out_path) {
   a.mask = (tsel_mask_t)mask;
   a.softmax_scale = 0.0f;
 
+  ws_lse = tsel_workspace_size(TSEL_OP_LSE, &a, &lay);
   ws_col = tsel_workspace_size(TSEL_OP_COLSCORE, &a, &lay);
+  ws_topk = tsel_workspace_size(TSEL_OP_TOPK, NULL, &lay);
   ws_cmp = tsel_workspace_size(TSEL_OP_COMPACT, NULL, &lay);
   ws_rope = tsel_workspace_size(TSEL_OP_MROPE, NULL, &lay);
-  if (ws_col == (size_t)-1 || ws_cmp == (size_t)-1 || ws_rope == (size_t)-1) return fail(tsel_last_error());
+  if (ws_lse == (size_t)-1 || ws_col == (size_t)-1 || ws_topk == (size_t)-1 || ws_cmp == (size_t)-1 ||
+      ws_rope == (size_t)-1)
+    return fail(tsel_last_error());
+  /* One buffer serves every call: the calls run one after another on one stream. */
   ws_bytes = ws_col > ws_cmp ? ws_col : ws_cmp;
   ws_bytes = ws_bytes > ws_rope ? ws_bytes : ws_rope;
+  ws_bytes = ws_bytes > ws_lse ? ws_bytes : ws_lse;
+  ws_bytes = ws_bytes > ws_topk ? ws_bytes : ws_topk;
   CHECK_HIP(hipMalloc(&ws, ws_bytes ? ws_bytes : 16));
   CHECK_HIP(hipMalloc((void **)&lse, sizeof(float) * (size_t)hq * T + 16));
   CHECK_HIP(hipMalloc((void **)&score, sizeof(float) * (size_t)N + 16));
   CHECK_HIP(hipMalloc((void **)&keep, (size_t)N + 16));
 
   /* The path: LSE -> column score -> budget -> compaction -> rotary positions. */
-  CHECK_TSEL(tsel_lse(&a, &lay, lse, stream));
+  CHECK_TSEL(tsel_lse(&a, &lay, lse, ws, ws_bytes, stream));
   CHECK_TSEL(tsel_colscore(&a, &lay, lse, score, ws, ws_bytes, stream));
   k_h = malloc(sizeof(int32_t) * B);
-  CHECK_TSEL(tsel_budget_topk(&lay, score, ratios, k_h, keep, stream));
+  CHECK_TSEL(tsel_budget_topk(&lay, score, ratios, k_h, keep, ws, ws_bytes, stream));
   t_out = 0;
   for (b = 0; b < B; ++b)
     t_out += (cu_seqlens[b + 1] - cu_seqlens[b]) - (cu_cands[cu_images[b + 1]] - cu_cands[cu_images[b]]) + k_h[b];

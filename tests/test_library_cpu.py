@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version(lib):
     header = open(HEADER).read()
     want = int(re.search(r"#define TSEL_VERSION (\d+)", header).group(1))
-    assert lib.tsel_version() == want == 3
+    assert lib.tsel_version() == want == 4
 
 
 FAKE = 4096  # non-null device address that validation never dereferences
@@ -91,8 +91,8 @@ def last_error(lib):
     return lib.tsel_last_error().decode()
 
 
-def call_lse(lib, a, lay, out=FAKE):
-    return lib.tsel_lse(ctypes.byref(a), ctypes.byref(lay.c), out, None)
+def call_lse(lib, a, lay, out=FAKE, ws=None, ws_bytes=0):
+    return lib.tsel_lse(ctypes.byref(a), ctypes.byref(lay.c), out, ws, ws_bytes, None)
 
 
 def test_attn_validation_codes(lib):
@@ -111,7 +111,7 @@ def test_attn_validation_codes(lib):
     # BLOCKDIAG needs every token inside an image.
     assert call_lse(lib, attn(mask=2), lay) == B.TSEL_EINVAL
     assert "BLOCKDIAG" in last_error(lib)
-    assert lib.tsel_lse(None, ctypes.byref(lay.c), FAKE, None) == B.TSEL_EINVAL
+    assert lib.tsel_lse(None, ctypes.byref(lay.c), FAKE, None, 0, None) == B.TSEL_EINVAL
     # fp8 inputs take whole 64-wide k chunks only.
     assert call_lse(lib, attn(dtype=B.TSEL_FP8_E4M3, d=96), lay) == B.TSEL_EUNSUPPORTED
     assert "fp8" in last_error(lib)
@@ -148,8 +148,57 @@ def test_topk_rejects_nan_ratio(lib):
     lay = good_layout()
     ratios = np.array([0.5, np.nan])
     k_h = np.zeros(2, np.int32)
-    rc = lib.tsel_budget_topk(ctypes.byref(lay.c), FAKE, ratios.ctypes.data, k_h.ctypes.data, FAKE, None)
+    rc = lib.tsel_budget_topk(ctypes.byref(lay.c), FAKE, ratios.ctypes.data, k_h.ctypes.data, FAKE, None, 0, None)
     assert rc == B.TSEL_EINVAL and "NaN" in last_error(lib)
+
+
+def test_layout_max_seqlen_checked_when_given(lib):
+    lay = good_layout()
+    lay.c.max_seqlen = 19  # the longest of the two requests (19 and 9 tokens)
+    assert lib.tsel_workspace_size(B.TSEL_OP_COMPACT, None, ctypes.byref(lay.c)) != ctypes.c_size_t(-1).value
+    lay.c.max_seqlen = 20
+    assert lib.tsel_workspace_size(B.TSEL_OP_COMPACT, None, ctypes.byref(lay.c)) == ctypes.c_size_t(-1).value
+    assert "max_seqlen" in last_error(lib)
+    lay.c.max_seqlen = 0  # not given
+    assert lib.tsel_workspace_size(B.TSEL_OP_COMPACT, None, ctypes.byref(lay.c)) != ctypes.c_size_t(-1).value
+
+
+def test_lse_key_split_workspace(lib):
+    """A small causal grid (one 3214-token request, 16 heads) splits its keys:
+    the LSE then needs Hq * T * (splits of the request) floats of workspace,
+    and a shortfall is refused before any launch.  A grid that fills the GPU
+    (the 16384-token layer, 64/8 heads) needs none."""
+    lay = HostLayout([0, 3214], [0, 12], [256 * i for i in range(12)], [[16, 16]] * 12,
+                     [256 * i for i in range(13)])
+    a = attn(hq=16, hkv=16, d=128)
+    need = lib.tsel_workspace_size(B.TSEL_OP_LSE, ctypes.byref(a), ctypes.byref(lay.c))
+    assert need > 0 and need % (16 * 3214 * 4) == 0
+    splits = need // (16 * 3214 * 4)
+    assert 2 <= splits <= 13
+    assert call_lse(lib, a, lay, ws=FAKE, ws_bytes=need - 4) == B.TSEL_EWORKSPACE
+    assert "workspace" in last_error(lib)
+    big = HostLayout([0, 16384], [0, 20], [750 * i for i in range(20)], [[25, 30]] * 20,
+                     [750 * i for i in range(21)])
+    assert lib.tsel_workspace_size(B.TSEL_OP_LSE, ctypes.byref(attn(hq=64, hkv=8, d=128)),
+                                   ctypes.byref(big.c)) == 0
+
+
+def test_topk_workspace_for_large_pools(lib):
+    """Pools above 32768 candidates are spread over blocks of 16384 and need
+    workspace (state and histograms of up to 64 such pools, plus one count
+    per block); pools that fit one workgroup need none."""
+    small = good_layout()
+    assert lib.tsel_workspace_size(B.TSEL_OP_TOPK, None, ctypes.byref(small.c)) == 0
+    lay = HostLayout([0, 40000, 140010], [0, 1, 2], [0, 40010], [[200, 200], [250, 400]],
+                     [0, 40000, 140000])
+    need = lib.tsel_workspace_size(B.TSEL_OP_TOPK, None, ctypes.byref(lay.c))
+    blocks = 3 + 7  # ceil(40000 / 16384) + ceil(100000 / 16384)
+    assert need == (64 * 4 + 64 * 256 + blocks) * 4
+    ratios = np.array([0.5, 0.5])
+    k_h = np.zeros(2, np.int32)
+    rc = lib.tsel_budget_topk(ctypes.byref(lay.c), FAKE, ratios.ctypes.data, k_h.ctypes.data, FAKE, FAKE,
+                              need - 4, None)
+    assert rc == B.TSEL_EWORKSPACE and "workspace" in last_error(lib)
 
 
 @pytest.mark.parametrize("tau,rmin,rmax,msg", [((0.5, np.nan), (0.0, 0.0), (1.0, 1.0), "NaN"),

@@ -250,6 +250,28 @@ def test_varlen_supplied_lse_full_size(dev):
     print(f"[check] {prob.B} pools, {prob.N} candidates compared; kept sets exact: {exact}", flush=True)
 
 
+@pytest.mark.parametrize("mask,dtype,hq,hkv,d", [("causal", "bf16", 16, 16, 128), ("full", "f16", 4, 2, 64),
+                                                  ("blockdiag", "bf16", 8, 8, 80), ("causal", "f32", 2, 1, 96)])
+def test_lse_key_split_matches_oracle(dev, mask, dtype, hq, hkv, d):
+    """Grids too small to fill the GPU split every row block's keys into
+    ranges whose partial log-sum-exps a merge pass combines; the split must
+    be in use here (nonzero LSE workspace) and every LSE, score and kept set
+    must match the oracle."""
+    if mask == "blockdiag":
+        reqs = [(3000, [(0, 30, 40), (1200, 25, 36), (2100, 30, 30)])]
+    else:
+        reqs = [(3214, [(256 * i, 16, 16) for i in range(12)]), (700, [(40, 20, 20)])]
+    prob = make_problem(f"lse_split_{mask}_{dtype}_h{hq}x{hkv}_d{d}", reqs, hq, hkv, d, dtype, mask,
+                        1.0 if mask != "causal" else 0.5, 63, ratio_range=(0.4, 0.9), emb_dim=32)
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    need = tsel.tsel_workspace_size(tsel.binding.TSEL_OP_LSE, lay, prob.q, prob.k, mask)
+    print(f"[check] LSE workspace {need} bytes = {need // (4 * hq * prob.T)} key splits", flush=True)
+    assert need > 0 and need % (4 * hq * prob.T) == 0
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, workers=oracle.default_workers(), with_emb=False), prob.emb)
+
+
 # Logit offsets (natural log) of a planted large-norm key above the ordinary
 # logits.  The LSE kernel sums exp2(c1*s - m) against m = (largest logit of
 # the first key tile) + 32 in log2 units, and redoes a workgroup exactly (max
@@ -333,6 +355,10 @@ def test_long_sequence_properties(dev):
     kept = int(out["keep"].sum())
     assert kept == int(out["k"][0]) == oracle.budget_k(0.5, T)
     assert int(out["compact"]["cu_seqlens"][-1]) == kept
+    # The 98304-candidate pool takes the many-block top-k: its kept set is
+    # exactly the oracle's top-k of the same (GPU) scores.
+    ref_keep, _ = oracle.topk(prob, out["score"].cpu().double().numpy())
+    assert np.array_equal(out["keep"].cpu().numpy(), ref_keep)
 
 
 # ---------------------------------------------------------------------------
@@ -531,6 +557,46 @@ def test_budget_topk_synthetic_scores_all_pool_sizes(dev, pattern):
         score[idx[2::3]] = -np.inf
     announce(prob)
     lay = tsel.Layout.from_problem(prob, dev)
+    keep, ks = tsel.tsel_budget_topk(lay, torch.from_numpy(score).to(dev), prob.keep_ratio)
+    torch.cuda.synchronize(dev)
+    ref_keep, ref_k = oracle.topk(prob, score.astype(np.float64))
+    assert np.array_equal(ks, ref_k)
+    assert np.array_equal(keep.cpu().numpy(), ref_keep)
+
+
+@pytest.mark.parametrize("pattern", ["distinct", "ties", "nonfinite"])
+def test_budget_topk_many_large_pools(dev, pattern):
+    """70 pools of 32769..40000 candidates (two launches of the many-block
+    top-k, 64 pools each at most) and one pool of 10^6, plus small pools in
+    between, on synthetic fp32 scores, against the oracle's rank rule
+    exactly; k from 0 to N."""
+    rng = np.random.default_rng(39)
+    reqs = []
+    for i in range(70):
+        n = int(rng.integers(32769, 40001))
+        side = 1
+        for f in range(int(np.sqrt(n)), 0, -1):
+            if n % f == 0:
+                side = f
+                break
+        reqs.append((n + 2, [(1, n // side, side)]))
+        if i % 10 == 3:
+            reqs.append((50, [(3, 5, 7)]))
+    reqs.append((1_000_000 + 5, [(5, 1000, 1000)]))
+    prob = make_problem("topk_many_large_" + pattern, reqs, 1, 1, 64, "bf16", "causal", 1.0, 40,
+                        ratio_range=(0.05, 0.95), emb_dim=4)
+    prob.keep_ratio[0], prob.keep_ratio[1], prob.keep_ratio[-1] = 0.0, 1.0, 0.37
+    score = (rng.random(prob.N) * 1e-4 + 3e-5).astype(np.float32)
+    if pattern == "ties":
+        score = np.round(score * 1e5).astype(np.float32) / np.float32(1e5)  # ~10 distinct values
+    if pattern == "nonfinite":
+        idx = rng.choice(prob.N, size=prob.N // 40, replace=False)
+        score[idx[0::3]] = np.nan
+        score[idx[1::3]] = np.inf
+        score[idx[2::3]] = -np.inf
+    announce(prob)
+    lay = tsel.Layout.from_problem(prob, dev)
+    assert tsel.tsel_workspace_size(tsel.binding.TSEL_OP_TOPK, lay) > 0
     keep, ks = tsel.tsel_budget_topk(lay, torch.from_numpy(score).to(dev), prob.keep_ratio)
     torch.cuda.synchronize(dev)
     ref_keep, ref_k = oracle.topk(prob, score.astype(np.float64))
