@@ -14,7 +14,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtsel.so")
+# TSEL_LIBRARY names another build of the same library (the host-sanitizer
+# build the CPU tests use); by default the in-tree libtsel.so.
+LIB_PATH = os.environ.get("TSEL_LIBRARY") or os.path.join(_HERE, "libtsel.so")
 
 TSEL_OK, TSEL_EINVAL, TSEL_EUNSUPPORTED, TSEL_EWORKSPACE, TSEL_EHIP = 0, -1, -2, -3, -4
 TSEL_F32, TSEL_F16, TSEL_BF16, TSEL_FP8_E4M3 = 0, 1, 2, 3

@@ -29,6 +29,22 @@ void clear_error() { g_err.clear(); }
 
 static int elem_size(int dt) { return dt == TSEL_F32 ? 4 : dt == TSEL_FP8_E4M3 ? 1 : 2; }
 
+// The ABI's enum fields hold whatever int the caller stored; reading them as
+// the enum type is undefined for values outside the enumerators, so they are
+// read as integers.
+static int dtype_of(const tsel_attn_t *a) {
+  int32_t v;
+  static_assert(sizeof(a->dtype) == sizeof(v), "enum fields are 32-bit");
+  memcpy(&v, &a->dtype, sizeof v);
+  return v;
+}
+static int mask_of(const tsel_attn_t *a) {
+  int32_t v;
+  static_assert(sizeof(a->mask) == sizeof(v), "enum fields are 32-bit");
+  memcpy(&v, &a->mask, sizeof v);
+  return v;
+}
+
 // With TSEL_DEBUG=1 in the environment, every call also checks that the
 // device layout arrays equal their host mirrors, through a synchronous
 // device-to-host copy (debugging only: otherwise the device arrays are
@@ -101,20 +117,20 @@ static int check_layout(const tsel_layout_t *l) {
 
 static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
   if (a == nullptr) return fail(TSEL_EINVAL, "attn is NULL");
-  if (a->dtype != TSEL_F32 && a->dtype != TSEL_F16 && a->dtype != TSEL_BF16 &&
-      a->dtype != TSEL_FP8_E4M3)
-    return fail(TSEL_EUNSUPPORTED, "dtype %d is not supported", (int)a->dtype);
+  if (dtype_of(a) != TSEL_F32 && dtype_of(a) != TSEL_F16 && dtype_of(a) != TSEL_BF16 &&
+      dtype_of(a) != TSEL_FP8_E4M3)
+    return fail(TSEL_EUNSUPPORTED, "dtype %d is not supported", dtype_of(a));
   if (a->head_dim != 64 && a->head_dim != 72 && a->head_dim != 80 && a->head_dim != 96 && a->head_dim != 128)
     return fail(TSEL_EUNSUPPORTED, "head_dim %d is not one of 64, 72, 80, 96, 128", a->head_dim);
-  if (a->dtype == TSEL_FP8_E4M3 && a->head_dim != 64 && a->head_dim != 128)
+  if (dtype_of(a) == TSEL_FP8_E4M3 && a->head_dim != 64 && a->head_dim != 128)
     return fail(TSEL_EUNSUPPORTED, "fp8 inputs need head_dim 64 or 128 (got %d)", a->head_dim);
   if (a->num_heads_q < 1 || a->num_heads_kv < 1 || a->num_heads_q % a->num_heads_kv != 0)
     return fail(TSEL_EINVAL, "num_heads_q (%d) must be a positive multiple of num_heads_kv (%d)",
                 a->num_heads_q, a->num_heads_kv);
-  if (a->mask != TSEL_MASK_FULL && a->mask != TSEL_MASK_CAUSAL && a->mask != TSEL_MASK_BLOCKDIAG)
-    return fail(TSEL_EINVAL, "mask %d is not valid", (int)a->mask);
+  if (mask_of(a) != TSEL_MASK_FULL && mask_of(a) != TSEL_MASK_CAUSAL && mask_of(a) != TSEL_MASK_BLOCKDIAG)
+    return fail(TSEL_EINVAL, "mask %d is not valid", mask_of(a));
   if (!isfinite(a->softmax_scale)) return fail(TSEL_EINVAL, "softmax_scale is not finite");
-  const int es = elem_size(a->dtype);
+  const int es = elem_size(dtype_of(a));
   if (l->total_tokens > 0) {
     if (a->q == nullptr || a->k == nullptr) return fail(TSEL_EINVAL, "q and k are required");
     if (((uintptr_t)a->q | (uintptr_t)a->k) & 15) return fail(TSEL_EINVAL, "q and k must be 16-byte aligned");
@@ -123,7 +139,7 @@ static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
   for (long long s : st)
     if (s <= 0 || (s * es) % 16 != 0)
       return fail(TSEL_EINVAL, "q/k strides must be positive and multiples of 16 bytes");
-  if (a->mask == TSEL_MASK_BLOCKDIAG) {
+  if (mask_of(a) == TSEL_MASK_BLOCKDIAG) {
     const long long n = l->cu_cands_h[l->num_images];
     if (n != l->total_tokens)
       return fail(TSEL_EINVAL, "BLOCKDIAG needs every token inside an image (%lld of %d are)", n,
@@ -136,7 +152,7 @@ static int check_attn(const tsel_attn_t *a, const tsel_layout_t *l) {
 // with 32-bit byte offsets from a per-tile base; those offsets must stay below
 // kBufferLimit.
 static int check_offsets(const tsel_attn_t *a, const tsel_layout_t *l, int F) {
-  const long long es = elem_size(a->dtype);
+  const long long es = elem_size(dtype_of(a));
   const long long k_span = 32LL * a->k_stride_tok * es;
   const long long q_span = ((32LL / F) * a->q_stride_tok + (long long)F * a->q_stride_head) * es;
   const long long l_span = ((long long)F * l->total_tokens + 32) * 4;
@@ -149,11 +165,11 @@ static void plan_common(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *
   const int hg = a->num_heads_q / a->num_heads_kv;
   int F = 1;
   while (F < 16 && hg % (F * 2) == 0) F *= 2;
-  p->dtype = a->dtype;
+  p->dtype = dtype_of(a);
   p->D = a->head_dim;
   p->F = F;
   p->nhb = a->num_heads_q / F;
-  p->segkind = (a->mask == TSEL_MASK_BLOCKDIAG) ? SEG_IMG : SEG_REQ;
+  p->segkind = (mask_of(a) == TSEL_MASK_BLOCKDIAG) ? SEG_IMG : SEG_REQ;
   p->nseg = (p->segkind == SEG_IMG) ? l->num_images : l->num_reqs;
 }
 
@@ -179,7 +195,7 @@ static void seg_sizes(const tsel_layout_t *l, int kind, int a, long long &n, lon
 int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   plan_common(a, l, p);
   if (int rc = check_offsets(a, l, p->F)) return rc;
-  const bool causal = a->mask == TSEL_MASK_CAUSAL;
+  const bool causal = mask_of(a) == TSEL_MASK_CAUSAL;
   // all: jobs launched; real: jobs that see at least one key.
   auto count = [&](int ng, int KS, long long &all, long long &real, long long &nmax) {
     const int TB = 4 * ng * 32 / p->F;
@@ -209,7 +225,7 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     p->total_jobs = all;
     p->jobs_per_hb = all / p->nhb;
   };
-  const int ng_max = max_groups(a->dtype, a->head_dim);
+  const int ng_max = max_groups(dtype_of(a), a->head_dim);
   long long all, real, nmax;
   count(ng_max, 0, all, real, nmax);
   if (all >= 512) {
@@ -275,7 +291,7 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     seg_sizes(l, p->segkind, s, n, nc);
     maxn = std::max(maxn, n);
   }
-  const int ng_max = max_groups(a->dtype, a->head_dim);
+  const int ng_max = max_groups(dtype_of(a), a->head_dim);
   auto plan_jobs = [&](int rc, int rcf) {
     long long J = 0;
     for (int s = 0; s < p->nseg; ++s) {
@@ -345,7 +361,7 @@ static DevLayout dev_layout(const tsel_layout_t *l) {
 // per job stands for its setup.
 static void job_weights(const tsel_attn_t *a, const tsel_layout_t *l, const AttnPlan &p, bool keyblocks,
                         std::vector<int> &w) {
-  const bool causal = a->mask == TSEL_MASK_CAUSAL;
+  const bool causal = mask_of(a) == TSEL_MASK_CAUSAL;
   w.clear();
   for (int s = 0; s < p.nseg; ++s) {
     long long lo, hi, sl, sh;
@@ -432,7 +448,7 @@ static AttnArgs attn_args(const tsel_attn_t *a, const tsel_layout_t *l, const At
   x.hg = a->num_heads_q / a->num_heads_kv;
   x.F = p.F;
   x.nhb = p.nhb;
-  x.causal = (a->mask == TSEL_MASK_CAUSAL) ? 1 : 0;
+  x.causal = (mask_of(a) == TSEL_MASK_CAUSAL) ? 1 : 0;
   x.segkind = p.segkind;
   x.nseg = p.nseg;
   const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / sqrt((double)a->head_dim);
@@ -739,9 +755,9 @@ int tsel_attention_fwd(const tsel_attn_t *attn, const tsel_layout_t *layout, con
   int rc = check_layout(layout);
   if (rc == TSEL_OK) rc = check_attn(attn, layout);
   if (rc != TSEL_OK) return rc;
-  if (attn->dtype != TSEL_BF16 && attn->dtype != TSEL_F16)
+  if (dtype_of(attn) != TSEL_BF16 && dtype_of(attn) != TSEL_F16)
     return fail(TSEL_EUNSUPPORTED, "the attention forward takes bf16 or f16 inputs");
-  const long long es = elem_size(attn->dtype);
+  const long long es = elem_size(dtype_of(attn));
   if (layout->total_tokens > 0) {
     if (v == nullptr || out == nullptr || lse == nullptr)
       return fail(TSEL_EINVAL, "v, out and lse are required");
