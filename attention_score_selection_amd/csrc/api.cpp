@@ -291,7 +291,7 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     seg_sizes(l, p->segkind, s, n, nc);
     maxn = std::max(maxn, n);
   }
-  const int ng_max = max_groups(dtype_of(a), a->head_dim);
+  const int ng_max = colscore_groups(dtype_of(a), a->head_dim);
   auto plan_jobs = [&](int rc, int rcf) {
     long long J = 0;
     for (int s = 0; s < p->nseg; ++s) {
@@ -306,7 +306,7 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
   };
   // Row chunks of 8192 query rows (RC tokens x F heads); halved while the
   // grid has fewer than 512 jobs (two workgroups per CU).
-  const int rc_full = std::max(32, 8192 / p->F);
+  const int rc_full = std::max(32, kChunkRows / p->F);
   for (int ng = ng_max;; ng = 1) {
     p->NT = ng;
     p->KB = 4 * ng * 32;
@@ -333,6 +333,11 @@ int plan_colscore(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     seg_sizes(l, p->segkind, s, n, nc);
     p->RCmax = std::max(p->RCmax, chunk_count((int)n, p->RC, p->RCF));
   }
+  // The kernel reads a chunk's query tiles through one buffer resource at
+  // 32-bit byte offsets from the chunk's first row.
+  const long long es = elem_size(dtype_of(a));
+  if (((long long)p->RC + 32) * a->q_stride_tok * es + (long long)p->F * a->q_stride_head * es >= kBufferLimit)
+    return fail(TSEL_EUNSUPPORTED, "q strides too large: a row chunk of %d tokens spans 2 GiB or more", p->RC);
   const long long N = l->cu_cands_h[l->num_images];
   p->partial_bytes = (size_t)p->nhb * p->RCmax * N * sizeof(float);
   if (p->total_jobs > (1LL << 30)) return fail(TSEL_EINVAL, "problem too large");

@@ -271,10 +271,12 @@ __global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
 // partial[(hb*RCmax + rc)*N + c].
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NG, bool ORD>
-__global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
+__global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
   using G = Geom<DT, D>;
-  constexpr int BUF = G::TILE + kRows * 4;  // tile + 32 floats of LSE (log2 units)
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) char smem[2 * G::TILE];
+  // LSE of the job's rows (a row chunk holds at most kChunkRows rows), in
+  // log2 units, padded to whole tiles with +inf.
+  __shared__ __attribute__((aligned(16))) float slse[kChunkRows + kRows];
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
@@ -345,56 +347,62 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<OR
     if (t == 0x7fffffff) return nullptr;
     return kbase + ((long long)t * a.k_st + (long long)g * a.k_sh) * G::ES;
   });
-  wait_vmem();
 
   const int tpt = kRows / F;  // tokens per streamed tile
   const int ntiles = uni((chunk_hi - row_lo + tpt - 1) / tpt);
-  // Query tile it: row r is (token row_lo + it*tpt + r/F, head h0 + r%F);
-  // rows of tokens from chunk_hi on are zero.
-  const char *qbase = reinterpret_cast<const char *>(a.q) + (long long)h0 * a.q_sh * G::ES;
+  // The job's LSE, row r = (token row_lo + r/F, head h0 + r%F), converted to
+  // log2 units; rows of tokens from chunk_hi on get +inf and so contribute
+  // exp2(-inf) = 0.
+  {
+    const long long T = a.L.T;
+    const float *lb = a.lse_in + (long long)h0 * T + row_lo;
+    const int nr = ntiles * kRows;
+    for (int r = threadIdx.x; r < nr; r += 256) {
+      const int dt = r / F;
+      slse[r] = row_lo + dt < chunk_hi ? lb[(long long)(r % F) * T + dt] * 1.44269504088896340736f : kPosInf;
+    }
+  }
+  // Query tile it: row r is (token row_lo + it*tpt + r/F, head h0 + r%F),
+  // read through one buffer resource at the byte offset of its first token.
   const long long qtok_bytes = a.q_st * G::ES;
   const int qhead_bytes = (int)(a.q_sh * G::ES);
-  auto tile_base = [&](int it) { return qbase + (long long)(row_lo + it * tpt) * qtok_bytes; };
-  auto tile_rows = [&](int it) { return (chunk_hi - (row_lo + it * tpt)) * F; };
-  // LSE of tile row r (threads 0..31): fetched one step ahead, converted to
-  // log2 units when staged; padding rows get +inf and so contribute
-  // exp2(-inf) = 0.
-  const long long T = a.L.T;
-  const float *lbase = a.lse_in + (long long)h0 * T;
-  const int loff = (int)(((threadIdx.x % F) * T + threadIdx.x / F) * 4);
-  auto lse_fetch = [&](int it) -> float {
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(lbase + row_lo + it * tpt);
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)threadIdx.x < tile_rows(it) ? loff : kOOB, 0, 0));
-  };
+  const __amdgpu_buffer_rsrc_t qrs =
+      buffer_rsrc(reinterpret_cast<const char *>(a.q) + ((long long)row_lo * a.q_st + (long long)h0 * a.q_sh) * G::ES);
+  const int tile_step = tpt * (int)qtok_bytes;
+  const int last_rows = (chunk_hi - (row_lo + (ntiles - 1) * tpt)) * F;
   float cs[NG];
 #pragma unroll
   for (int n = 0; n < NG; ++n) cs[n] = 0.f;
 
   StageDirect<DT, D> st;
   st.init([&](int r) { return (r / F) * (int)qtok_bytes + (r % F) * qhead_bytes; });
-  auto buf = [&](int it) { return smem + (it & 1) * BUF; };
-  auto stage_lse = [&](int it, float v) {
-    if (threadIdx.x < kRows)
-      reinterpret_cast<float *>(buf(it) + G::TILE)[threadIdx.x] =
-          (int)threadIdx.x < tile_rows(it) ? v * 1.44269504088896340736f : kPosInf;
+  auto buf = [&](int it) { return smem + (it & 1) * G::TILE; };
+  auto load = [&](int it) {
+    if (it + 1 < ntiles) st.template load_at<false>(buf(it), qrs, it * tile_step, kRows);
+    else st.template load_at<true>(buf(it), qrs, it * tile_step, last_rows);
   };
-  float lreg = 0.f;
-  st.load(buf(0), tile_base(0), tile_rows(0));
-  if (threadIdx.x < kRows) lreg = lse_fetch(0);
-  stage_lse(0, lreg);
-  if (ntiles > 1 && threadIdx.x < kRows) lreg = lse_fetch(1);
+  load(0);
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+
+  // Tiles in three runs for this wave (causal): every row before every key
+  // (skipped), rows that reach some key of the wave (masked where a group's
+  // last key is later than the tile's first row), then rows past all its
+  // keys.  Every wave runs every tile's barrier and load.
+  const int skip_end = a.causal ? uni(min(ntiles, max(0, (wkmin - row_lo) / tpt))) : 0;
+  const int full_start =
+      a.causal ? uni(min(ntiles, max(skip_end, (wkmax - row_lo + tpt - 1) / tpt))) : 0;
+
+  // One tile: refill the other buffer (read last step), then the MFMAs and
+  // the epilogue of this tile (MODE 0: skipped, 1: masked, 2: unmasked).
+  auto step = [&](int it, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
     const char *b = buf(it);
-    const int tt0 = row_lo + it * tpt;
-    const bool run = !(a.causal && tt0 + tpt - 1 < wkmin);  // otherwise every row precedes every key
     Chunk<DT> af[G::KCH];
     float l2[16];
-    if (run) {
+    if (MODE != 0) {
       read_frag<DT, D>(af, b);
       // LSE of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3.
-      const float *lb = reinterpret_cast<const float *>(b + G::TILE) + 4 * (lane >> 5);
+      const float *lb = slse + it * kRows + 4 * (lane >> 5);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
@@ -402,16 +410,11 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<OR
         for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
       }
     }
-    // The other buffer was last read in the previous step: refill it now.
-    if (it + 1 < ntiles) {
-      st.load(buf(it + 1), tile_base(it + 1), tile_rows(it + 1));
-      stage_lse(it + 1, lreg);
-      if (it + 2 < ntiles && threadIdx.x < kRows) lreg = lse_fetch(it + 2);
-    }
-    if (run) {
+    if (it + 1 < ntiles) load(it + 1);
+    if (MODE != 0) {
       f32x16 s[NG];
       tile_mma<DT, D, NG>(af, kf, s);
-      // Causal: a row sees a key only if the key's token is not later.
+      const int tt0 = row_lo + it * tpt;
       auto epi = [&](int n, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         // Row of register v has token tt0 + (acc_row_c(v) + 4*(lane/32)) / F;
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<OR
         }
         cs[n] += tree16(p);
       };
-      if (!a.causal || tt0 >= wkmax) {
+      if (MODE == 2) {
 #pragma unroll
         for (int n = 0; n < NG; ++n) epi(n, std::false_type{});
       } else {
@@ -439,8 +442,17 @@ __global__ __launch_bounds__(256, 2) void colscore_kernel(AttnArgs a, PermArg<OR
         }
       }
     }
+    // The barrier (and its wait for the next tile's load) stays after this
+    // tile's MFMAs and epilogue: the scheduler would otherwise hoist it above
+    // them in the branch-free runs and expose the load's latency.
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-  }
+  };
+  int it = 0;
+  for (; it < skip_end; ++it) step(it, std::integral_constant<int, 0>{});
+  for (; it < full_start; ++it) step(it, std::integral_constant<int, 1>{});
+  for (; it < ntiles; ++it) step(it, std::integral_constant<int, 2>{});
+
   float *out = a.partial + ((long long)hb * a.RCmax + rc) * a.N;
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
@@ -501,6 +513,8 @@ namespace {
 
 template <int DT, int D>
 constexpr int kNGMax = max_groups(DT, D);
+template <int DT, int D>
+constexpr int kColNG = colscore_groups(DT, D);
 
 // The permuted variants exist for the widest group count only (the
 // one-group fallback serves small grids, where order matters little).
@@ -522,7 +536,7 @@ hipError_t lse_go(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hip
 template <int DT, int D, int NG>
 hipError_t col_go(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
   const int grid = (int)((p.total_jobs + 7) / 8 * 8);
-  if constexpr (NG == kNGMax<DT, D>) {
+  if constexpr (NG == kColNG<DT, D>) {
     if (perm != nullptr) {
       hipLaunchKernelGGL((colscore_kernel<DT, D, NG, true>), dim3(grid), dim3(256), 0, s, a,
                          PermArg<true>{*perm});
@@ -542,7 +556,7 @@ hipError_t lse_ng(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hip
 }
 template <int DT, int D>
 hipError_t col_ng(const AttnPlan &p, const AttnArgs &a, const JobPerm *perm, hipStream_t s) {
-  if (p.NT == kNGMax<DT, D>) return col_go<DT, D, kNGMax<DT, D>>(p, a, perm, s);
+  if (p.NT == kColNG<DT, D>) return col_go<DT, D, kColNG<DT, D>>(p, a, perm, s);
   return col_go<DT, D, 1>(p, a, perm, s);
 }
 

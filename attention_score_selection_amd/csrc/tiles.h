@@ -218,6 +218,24 @@ struct StageDirect {
       }
     }
   }
+  // Start the copy of the tile at byte `soff` past the resource's base into
+  // `tile` (tile rows [0, nvalid) when PART, else all 32 rows); the rest of
+  // the tile reads as zero.  Every wave but the last of a partial block row
+  // issues the same loads, so only the last block needs a (wave-uniform)
+  // test.  Complete once this wave's vector-memory counter drains.
+  template <bool PART>
+  __device__ __forceinline__ void load_at(char *tile, __amdgpu_buffer_rsrc_t rs, int soff, int nvalid) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int w = uni(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int blk = 4 * j + w;
+      if (j < BPW - 1 || blk < G::NBLK)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(tile + blk * 1024), 16,
+                                                 (!PART || row[j] < nvalid) ? off[j] : kOOB, soff, 0, 0);
+    }
+#endif
+  }
   // Start the copy of tile rows [0, nvalid) from `base` (wave-uniform) into
   // `tile`; the rest of the tile reads as zero.  Complete once this wave's
   // vector-memory counter drains (a __syncthreads() waits for that).
