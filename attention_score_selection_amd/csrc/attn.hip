@@ -39,75 +39,83 @@ namespace tsel {
 // tiles of 32 over [seg_lo, key_hi).
 // ---------------------------------------------------------------------------
 
-// One pass over key tiles [t0, t1).  MAXMODE: acc = running max of the raw
-// logit over this lane's keys.  Otherwise acc = running sum of
+// One pass over the job's key tiles [0, nt): tile it holds keys key_lo + 32*it
+// .. +31 (those from key_hi on read as zero).  Tiles [0, full_end) are
+// visible to every row of this wave, tiles [full_end, seen_end) to some of
+// them (masked per lane), tiles from seen_end on to none (skipped; the wave
+// still stages them and joins every barrier).  MAXMODE: acc = running max of
+// the raw logit over this lane's keys.  Otherwise acc = running sum of
 // exp2(c1*s - m) over this lane's keys.
 template <int DT, int D, int NG, bool MAXMODE>
-__device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, int g, int key_lo,
-                                         int key_hi, int t0, int t1,
+__device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageRegs<DT, D> &st,
+                                         const char *kbase, int tile_bytes, int key_lo, int key_hi, int nt,
+                                         int full_end, int seen_end,
                                          const Chunk<DT> (&qf)[NG][kch(DT, D)],
-                                         const int (&qtok)[NG],
-                                         int wtok_min, int wtok_max, const float (&m)[NG],
+                                         const int (&qtok)[NG], const float (&m)[NG],
                                          float (&acc)[NG]) {
   using G = Geom<DT, D>;
-  // Key tile it: rows key_lo + 32*it + r of KV head g; rows from key_hi on are zero.
-  const char *kbase = reinterpret_cast<const char *>(a.k) + (long long)g * a.k_sh * G::ES;
-  const long long krow = a.k_st * G::ES;
-  auto tile_base = [&](int it) { return kbase + (long long)(key_lo + kRows * it) * krow; };
-  auto tile_rows = [&](int it) { return key_hi - (key_lo + kRows * it); };
 #pragma unroll
   for (int n = 0; n < NG; ++n) acc[n] = MAXMODE ? kNegInf : 0.0f;
-
-  StageRegs<DT, D> st;
-  st.init([&](int r) { return r * (int)krow; });
-  st.load(tile_base(t0), tile_rows(t0));
+  // Key tile it from its first row on (one scalar base per tile, so the
+  // key range of a job is not limited by the 32-bit buffer offsets).
+  auto load = [&](int it) {
+    const char *p = kbase + (long long)it * tile_bytes;
+    const int nv = key_hi - (key_lo + kRows * it);
+    if (nv >= kRows) st.template load<false>(p, kRows);
+    else st.template load<true>(p, nv);
+  };
+  load(0);
   st.store(smem);
-  if (t0 + 1 < t1) st.load(tile_base(t0 + 1), tile_rows(t0 + 1));
+  if (nt > 1) load(1);
   __syncthreads();
-  for (int it = t0; it < t1; ++it) {
-    const char *tile = smem + ((it - t0) & 1) * G::TILE;
-    const int k0 = key_lo + kRows * it;
-    if (!(a.causal && k0 > wtok_max)) {  // otherwise no row of this wave sees the tile
+
+  // One tile (MODE 0: skipped, 1: masked, 2: visible to every row).
+  auto step = [&](int it, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    if (MODE != 0) {
+      const char *tile = smem + (it & 1) * G::TILE;
+      const int k0 = key_lo + kRows * it;
       Chunk<DT> af[G::KCH];
       read_frag<DT, D>(af, tile);
       f32x16 s[NG];
       tile_mma<DT, D, NG>(af, qf, s);
-      // Keys past the segment end or (causal) past a row's token are invisible.
-      auto epi = [&](auto masked) {
-        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-        for (int n = 0; n < NG; ++n) {
-          // Key of register v is k0 + acc_row_c(v) + 4*(lane/32): visible while
-          // below key_hi and (causal) not past the row's token qtok[n].
-          const int lim = MASKED ? min(key_hi - 1, a.causal ? qtok[n] : key_hi - 1) -
-                                       (k0 + 4 * (lane_id() >> 5))
-                                 : 0;
-          float p[16];
+      for (int n = 0; n < NG; ++n) {
+        // Key of register v is k0 + acc_row_c(v) + 4*(lane/32): visible while
+        // below key_hi and (causal) not past the row's token qtok[n].
+        const int lim = MODE == 1 ? min(key_hi - 1, a.causal ? qtok[n] : key_hi - 1) -
+                                        (k0 + 4 * (lane_id() >> 5))
+                                  : 0;
+        float p[16];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const bool vis = !MASKED || acc_row_c(v) <= lim;
-            if (MAXMODE) p[v] = vis ? s[n][v] : kNegInf;
-            else p[v] = vis ? fast_exp2(fmaf(s[n][v], a.c1, -m[n])) : 0.0f;
-          }
-          if (MAXMODE) {
-            float t = p[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) t = fmaxf(t, p[v]);
-            acc[n] = fmaxf(acc[n], t);
-          } else {
-            acc[n] += tree16(p);
-          }
+        for (int v = 0; v < 16; ++v) {
+          const bool vis = MODE == 2 || acc_row_c(v) <= lim;
+          if (MAXMODE) p[v] = vis ? s[n][v] : kNegInf;
+          else p[v] = vis ? fast_exp2(fmaf(s[n][v], a.c1, -m[n])) : 0.0f;
         }
-      };
-      if ((k0 + kRows > key_hi) || (a.causal && k0 + kRows - 1 > wtok_min)) epi(std::true_type{});
-      else epi(std::false_type{});
+        if (MAXMODE) {
+          float t = p[0];
+#pragma unroll
+          for (int v = 1; v < 16; ++v) t = fmaxf(t, p[v]);
+          acc[n] = fmaxf(acc[n], t);
+        } else {
+          acc[n] += tree16(p);
+        }
+      }
     }
-    if (it + 1 < t1) {
-      st.store(smem + ((it + 1 - t0) & 1) * G::TILE);
-      if (it + 2 < t1) st.load(tile_base(it + 2), tile_rows(it + 2));
+    if (it + 1 < nt) {
+      st.store(smem + ((it + 1) & 1) * G::TILE);
+      if (it + 2 < nt) load(it + 2);
     }
+    // Keep the barrier after this tile's MFMAs and epilogue (the scheduler
+    // would otherwise hoist it above them in the branch-free runs).
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-  }
+  };
+  int it = 0;
+  for (; it < full_end; ++it) step(it, std::integral_constant<int, 2>{});
+  for (; it < seen_end; ++it) step(it, std::integral_constant<int, 1>{});
+  for (; it < nt; ++it) step(it, std::integral_constant<int, 0>{});
 }
 
 // Kernel argument carrying the job permutation (ORD) or nothing.
@@ -158,16 +166,30 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
 
   const int lane = lane_id(), w = uni(threadIdx.x >> 6);
   const int F = a.F;
-  const int wtok0 = tok_lo + w * (NG * kRows / F);
-  const int wtok_max = wtok0 + NG * kRows / F - 1;
-  const int h0 = hb * F;
-  const int g = h0 / a.hg;
+  const int wtok0 = uni(tok_lo + w * (NG * kRows / F));
+  const int wtok_max = uni(wtok0 + NG * kRows / F - 1);
+  const int h0 = uni(hb * F);
+  const int g = uni(h0 / a.hg);
   // Keys of this job: the row block's whole range, or its ks-th split.
-  const int key_lo = seg_lo + ks * KS;
+  const int key_lo = uni(seg_lo + ks * KS);
   const int key_end = a.causal ? tok_hi : seg_hi;
-  const int key_hi = KS ? min(key_end, key_lo + KS) : key_end;
+  const int key_hi = uni(KS ? min(key_end, key_lo + KS) : key_end);
   if (key_lo >= key_hi) return;  // a causal row block before this split
-  const int ntiles = (key_hi - key_lo + kRows - 1) / kRows;
+  const int ntiles = uni((key_hi - key_lo + kRows - 1) / kRows);
+  // Tiles every row of this wave sees in full, and tiles some row sees
+  // (causal: keys up to the wave's last token); a wave past the row block's
+  // end sees none.
+  auto tiles_upto = [&](int last_key) {  // tiles whose keys all lie at or before last_key
+    const int x = last_key - key_lo - (kRows - 1);
+    return x < 0 ? 0 : min(ntiles, x / kRows + 1);
+  };
+  auto tiles_from = [&](int last_key) {  // tiles whose first key lies at or before last_key
+    const int x = last_key - key_lo;
+    return x < 0 ? 0 : min(ntiles, x / kRows + 1);
+  };
+  const bool wave_live = wtok0 < tok_hi;
+  const int full_end = uni(wave_live ? tiles_upto(a.causal ? min(key_hi - 1, wtok0) : key_hi - 1) : 0);
+  const int seen_end = uni(wave_live ? (a.causal ? tiles_from(wtok_max) : ntiles) : 0);
 
   // Resident queries: row q of this wave is (token wtok0 + q / F, head h0 + q % F).
   Chunk<DT> qf[NG][G::KCH];
@@ -182,6 +204,13 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
   for (int n = 0; n < NG; ++n) qtok[n] = wtok0 + (n * kRows + (lane & 31)) / F;
   wait_vmem();
 
+  // Key tile it starts at key row key_lo + 32*it of KV head g.
+  const long long krow = a.k_st * G::ES;
+  const char *kbase = reinterpret_cast<const char *>(a.k) + (long long)g * a.k_sh * G::ES + key_lo * krow;
+  const int tile_bytes = (int)(kRows * krow);
+  StageRegs<DT, D> st;
+  st.init([&](int r) { return r * (int)krow; });
+
   // Offset m: max logit of the first key tile (which every row sees, except,
   // in a later key split of a causal row block, the rows before the split)
   // plus 32 (log2 units); the sum pass then cannot overflow unless a later
@@ -190,10 +219,12 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
 #pragma unroll
   for (int n = 0; n < NG; ++n) m[n] = 0.f;
   if (threadIdx.x == 0) s_bad = 0;
-  lse_pass<DT, D, NG, true>(smem, a, g, key_lo, key_hi, 0, 1, qf, qtok, wtok0, wtok_max, m, acc);
+  lse_pass<DT, D, NG, true>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, 1, min(full_end, 1), min(seen_end, 1),
+                            qf, qtok, m, acc);
 #pragma unroll
   for (int n = 0; n < NG; ++n) m[n] = fmaxf(acc[n], __shfl_xor(acc[n], 32, 64)) * a.c1 + 32.0f;
-  lse_pass<DT, D, NG, false>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
+  lse_pass<DT, D, NG, false>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, ntiles, full_end, seen_end, qf, qtok,
+                             m, acc);
   float tot[NG];
   bool ok = true;
 #pragma unroll
@@ -206,11 +237,12 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
   __syncthreads();
   if (s_bad) {
     // Exact two-pass fallback: true row max, then the sum against it.
-    lse_pass<DT, D, NG, true>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m, acc);
+    lse_pass<DT, D, NG, true>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, ntiles, full_end, seen_end, qf,
+                              qtok, m, acc);
 #pragma unroll
     for (int n = 0; n < NG; ++n) m[n] = fmaxf(acc[n], __shfl_xor(acc[n], 32, 64)) * a.c1;
-    lse_pass<DT, D, NG, false>(smem, a, g, key_lo, key_hi, 0, ntiles, qf, qtok, wtok0, wtok_max, m,
-                               acc);
+    lse_pass<DT, D, NG, false>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, ntiles, full_end, seen_end, qf,
+                               qtok, m, acc);
 #pragma unroll
     for (int n = 0; n < NG; ++n) tot[n] = acc[n] + __shfl_xor(acc[n], 32, 64);
   }

@@ -166,19 +166,21 @@ struct StageRegs {
       }
     }
   }
-  // Tile rows [0, nvalid) come from `base` (wave-uniform), the rest are zero.
+  // Tile rows [0, nvalid) come from `base` (wave-uniform), the rest are zero;
+  // without PART all 32 rows are valid (units past the tile still read zero).
+  template <bool PART = true>
   __device__ __forceinline__ void load(const char *base, int nvalid) {
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base);
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i)
       r[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, row[i] < nvalid ? off[i] : kOOB, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (!PART || row[i] < nvalid) ? off[i] : kOOB, 0, 0));
   }
   __device__ __forceinline__ void store(char *tile) const {
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
       const int u = threadIdx.x + 256 * i;
-      if (u < kRows * G::UNITS) {
+      if (kRows * G::UNITS == 256 * G::UPT || u < kRows * G::UNITS) {  // (every unit is real when the tile fills the threads)
         const int rr = u / G::UNITS, col = u % G::UNITS;
         *reinterpret_cast<uint4 *>(tile + rr * G::RS + col * 16) = r[i];
       }
