@@ -23,11 +23,9 @@
 // Query heads that share a KV head are folded into the row dimension (F heads
 // per token in each 32-row group), so one key fragment serves F query heads.
 //
-// Streamed tiles reach LDS through buffer loads whose per-lane offsets are
-// fixed for the whole job: the LSE pass stages through registers (one tile
-// ahead), the column-score pass uses the LDS-direct form of the buffer load
-// (no staging registers; measured faster there, while the LSE pass measured
-// slightly faster with register staging).
+// Streamed tiles reach LDS through the LDS-direct form of the buffer load (no
+// staging registers), one tile ahead, with per-lane offsets fixed for the
+// whole job.
 #include "tiles.h"
 
 namespace tsel {
@@ -47,7 +45,7 @@ namespace tsel {
 // the raw logit over this lane's keys.  Otherwise acc = running sum of
 // exp2(c1*s - m) over this lane's keys.
 template <int DT, int D, int NG, bool MAXMODE>
-__device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageRegs<DT, D> &st,
+__device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageDirect<DT, D> &st,
                                          const char *kbase, int tile_bytes, int key_lo, int key_hi, int nt,
                                          int full_end, int seen_end,
                                          const Chunk<DT> (&qf)[NG][kch(DT, D)],
@@ -59,24 +57,23 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageReg
   // Key tile it from its first row on (one scalar base per tile, so the
   // key range of a job is not limited by the 32-bit buffer offsets).
   auto load = [&](int it) {
-    const char *p = kbase + (long long)it * tile_bytes;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(kbase + (long long)it * tile_bytes);
     const int nv = key_hi - (key_lo + kRows * it);
-    if (nv >= kRows) st.template load<false>(p, kRows);
-    else st.template load<true>(p, nv);
+    char *b = smem + (it & 1) * G::TILE;
+    if (nv >= kRows) st.template load_at<false>(b, rs, 0, kRows);
+    else st.template load_at<true>(b, rs, 0, nv);
   };
   load(0);
-  st.store(smem);
-  if (nt > 1) load(1);
   __syncthreads();
 
   // One tile (MODE 0: skipped, 1: masked, 2: visible to every row).
   auto step = [&](int it, auto mode) {
     constexpr int MODE = decltype(mode)::value;
+    Chunk<DT> af[G::KCH];
+    if (MODE != 0) read_frag<DT, D>(af, smem + (it & 1) * G::TILE);
+    if (it + 1 < nt) load(it + 1);
     if (MODE != 0) {
-      const char *tile = smem + (it & 1) * G::TILE;
       const int k0 = key_lo + kRows * it;
-      Chunk<DT> af[G::KCH];
-      read_frag<DT, D>(af, tile);
       f32x16 s[NG];
       tile_mma<DT, D, NG>(af, qf, s);
 #pragma unroll
@@ -102,10 +99,6 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageReg
           acc[n] += tree16(p);
         }
       }
-    }
-    if (it + 1 < nt) {
-      st.store(smem + ((it + 1) & 1) * G::TILE);
-      if (it + 2 < nt) load(it + 2);
     }
     // Keep the barrier after this tile's MFMAs and epilogue (the scheduler
     // would otherwise hoist it above them in the branch-free runs).
@@ -208,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
   const long long krow = a.k_st * G::ES;
   const char *kbase = reinterpret_cast<const char *>(a.k) + (long long)g * a.k_sh * G::ES + key_lo * krow;
   const int tile_bytes = (int)(kRows * krow);
-  StageRegs<DT, D> st;
+  StageDirect<DT, D> st;
   st.init([&](int r) { return r * (int)krow; });
 
   // Offset m: max logit of the first key tile (which every row sees, except,
