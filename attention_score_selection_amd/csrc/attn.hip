@@ -382,9 +382,22 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     const long long T = a.L.T;
     const float *lb = a.lse_in + (long long)h0 * T + row_lo;
     const int nr = ntiles * kRows;
-    for (int r = threadIdx.x; r < nr; r += 256) {
-      const int dt = r / F;
-      slse[r] = row_lo + dt < chunk_hi ? lb[(long long)(r % F) * T + dt] * 1.44269504088896340736f : kPosInf;
+    const int dmax = chunk_hi - 1 - row_lo;   // last token offset of the chunk
+    const int lf = 31 - __builtin_clz(F);     // F is a power of two
+    // Batches of eight independent loads per thread (token offsets clamped
+    // into the chunk, so every address is valid), then the stores.
+    for (int r0 = 0; r0 < nr; r0 += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + 256 * u + (int)threadIdx.x;
+        v[u] = lb[(long long)(r & (F - 1)) * T + min(r >> lf, dmax)];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + 256 * u + (int)threadIdx.x;
+        if (r < nr) slse[r] = (r >> lf) <= dmax ? v[u] * 1.44269504088896340736f : kPosInf;
+      }
     }
   }
   // Query tile it: row r is (token row_lo + it*tpt + r/F, head h0 + r%F),
