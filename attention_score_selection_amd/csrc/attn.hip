@@ -336,7 +336,11 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
   chunk_range(rc, seg_hi - seg_lo, a.RC, a.RCF, chunk_lo, chunk_hi);
   chunk_lo = uni(seg_lo + chunk_lo);
   chunk_hi = uni(seg_lo + chunk_hi);
-  const int first_ktok = uni(cand_token(a.L, s_lo, s_hi, kb0));
+  // Candidate -> token lookups of this job.
+  const ImgLanes im = img_lanes(a.L, s_lo, s_hi);
+  const bool few = im.n <= 64;
+  auto tok_u = [&](int c) { return uni(few ? img_token_uniform(im, c) : cand_token(a.L, s_lo, s_hi, c)); };
+  const int first_ktok = tok_u(kb0);
   const int row_lo = uni(a.causal ? max(chunk_lo, first_ktok) : chunk_lo);
   if (row_lo >= chunk_hi) return;  // no row of this chunk sees any key of the block
 
@@ -347,8 +351,8 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
   const int wc0 = kb0 + w * NG * kRows;
   const int wlast = min(wc0 + NG * kRows, kb1) - 1;
   // Smallest and largest key token of this wave (candidates are in token order).
-  const int wkmax = uni((wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wlast) : -1);
-  const int wkmin = uni((wlast >= wc0) ? cand_token(a.L, s_lo, s_hi, wc0) : 0x7fffffff);
+  const int wkmax = (wlast >= wc0) ? tok_u(wlast) : -1;
+  const int wkmin = (wlast >= wc0) ? tok_u(wc0) : 0x7fffffff;
 
   // Resident keys: group n, lane column lane % 32 is candidate wc0 + 32n + lane % 32.
   Chunk<DT> kf[NG][G::KCH];
@@ -356,7 +360,8 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
     const int c = wc0 + n * kRows + (lane & 31);
-    ktok[n] = (c < kb1) ? cand_token(a.L, s_lo, s_hi, c) : 0x7fffffff;
+    const int t = few ? img_token(im, min(c, kb1 - 1)) : cand_token(a.L, s_lo, s_hi, min(c, kb1 - 1));
+    ktok[n] = (c < kb1) ? t : 0x7fffffff;
   }
   // Largest key token of each group (its last candidate before kb1; INT_MAX
   // marks an empty group, which then always takes the masked path).

@@ -83,6 +83,38 @@ __device__ __forceinline__ int cand_token(const DevLayout &L, int s_lo, int s_hi
   return L.img_start[s] + (c - L.cu_cands[s]);
 }
 
+// The images [s_lo, s_hi) of a segment spread over the lanes of a wave, one
+// image per lane, when there are at most 64: the candidate -> token lookup
+// then needs one round of loads for the whole job instead of a binary search
+// through memory per lookup.  All 64 lanes must call these.
+struct ImgLanes {
+  int n;      // images (wave-uniform); more than 64: use cand_token instead
+  int cand0;  // lane i < n: first candidate of image s_lo + i (INT_MAX past n)
+  int tok0;   // lane i < n: first token of image s_lo + i
+};
+__device__ __forceinline__ ImgLanes img_lanes(const DevLayout &L, int s_lo, int s_hi) {
+  ImgLanes t;
+  t.n = s_hi - s_lo;
+  const int i = lane_id();
+  const bool in = i < t.n;
+  t.cand0 = in ? L.cu_cands[s_lo + i] : 0x7fffffff;
+  t.tok0 = in ? L.img_start[s_lo + i] : 0;
+  return t;
+}
+// Token of candidate c of the segment, c wave-uniform: its image is the last
+// one whose first candidate is at or before c.
+__device__ __forceinline__ int img_token_uniform(const ImgLanes &t, int c) {
+  const unsigned long long m = __ballot(t.cand0 <= c);
+  const int s = 63 - __builtin_clzll(m);
+  return __builtin_amdgcn_readlane(t.tok0, s) + c - __builtin_amdgcn_readlane(t.cand0, s);
+}
+// The same for a per-lane candidate c.
+__device__ __forceinline__ int img_token(const ImgLanes &t, int c) {
+  int s = 0;
+  for (int j = 1; j < t.n; ++j) s += __builtin_amdgcn_readlane(t.cand0, j) <= c ? 1 : 0;
+  return __shfl(t.tok0, s, 64) + c - __shfl(t.cand0, s, 64);
+}
+
 // Find which segment owns item `idx` when segment a owns count(a) items,
 // segments in order.  Wave-uniform; all 64 lanes must call it.  Returns the
 // segment, and the item's index inside it in `local`; returns -1 if idx is

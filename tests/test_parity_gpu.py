@@ -465,6 +465,29 @@ def test_tiny_images_blockdiag(dev):
     P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
 
 
+@pytest.mark.parametrize("n_img", [64, 65, 90])
+def test_many_images_in_one_request(dev, n_img):
+    """One causal request holding n_img small images (2x3, 1x4, ...) between
+    text runs: the column score maps candidates to tokens through a per-lane
+    image table when a segment has at most 64 images and through a search of
+    the layout beyond that; both against the oracle, with GQA and a second
+    request after the first."""
+    rng = np.random.default_rng(200 + n_img)
+    imgs, t = [], 0
+    for i in range(n_img):
+        t += int(rng.integers(0, 3))
+        h, w = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        imgs.append((t, h, w))
+        t += h * w
+    n0 = t + 5
+    reqs = [(n0, imgs), (40, [(3, 4, 4)])]
+    prob = make_problem(f"many_images_{n_img}", reqs, 8, 2, 64, "bf16", "causal", 1.0, 300 + n_img,
+                        ratios=0.5, emb_dim=16)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
 def test_nonfinite_inputs_rank_last(dev):
     """A NaN in one query row poisons the LSE of that row and the scores of
     every candidate the row sees; those rank as -inf, identically on both sides."""
