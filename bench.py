@@ -210,6 +210,32 @@ def time_gemm(n, dev, stream, args):
             "library": "torch.matmul (hipBLASLt), bf16 in and out, fp32 accumulate"}
 
 
+def calib_suite(dev):
+    """Kernels whose HBM traffic is known, run once each in this order (a
+    counter pass lists their dispatches last): device-to-device copies (read
+    and write n bytes), a sum (reads 1 GiB), a fill (writes 1 GiB)."""
+    import torch
+    ops = []
+    for mb in (16, 64, 256, 1024):
+        n = mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        ops.append({"op": f"copy {mb} MiB", "read": n, "write": n})
+        del src, dst
+    x = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize(dev)
+    float(x.sum())
+    ops.append({"op": "sum 1 GiB fp32", "read": 1 << 30, "write": 0})
+    x.fill_(2.0)
+    torch.cuda.synchronize(dev)
+    ops.append({"op": "fill 1 GiB fp32", "read": 0, "write": 1 << 30})
+    del x
+    return ops
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +244,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
+    ap.add_argument("--calib-suite", action="store_true",
+                    help="after timing, run kernels of known traffic once each (device copies of 16, "
+                         "64, 256 and 1024 MiB, a 1 GiB read-only sum, a 1 GiB fill), to check how "
+                         "the HBM byte counters relate to real traffic")
     ap.add_argument("--calib-gemm", type=int, default=0,
                     help="also time a plain n x n x n bf16 matrix product (torch.matmul, i.e. the "
                          "vendor GEMM library) on random data: the MFMA rate a dense library "
@@ -274,7 +304,7 @@ def main():
     ws_topk = torch.empty((max(16, tsel.tsel_workspace_size(2, lay)),), dtype=torch.uint8, device=dev)
     _, ks = tsel.tsel_budget_topk(
         lay, tsel.tsel_colscore(q, k, lay, prob.mask, tsel.tsel_lse(q, k, lay, prob.mask, scale), scale),
-        ratios)
+        ratios, out=keep)
     outs = {}
     tsel.tsel_compact(lay, keep, ks, emb, workspace=ws_cmp, outputs=outs)
     t_out = int(outs["token_idx"].numel())
@@ -404,6 +434,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize(dev)
         result["calib_copy_bytes"] = n
+    if args.calib_suite:
+        result["calib_suite"] = calib_suite(dev)
     if args.calib_gemm > 0:
         result["calib_gemm"] = time_gemm(args.calib_gemm, dev, stream, args)
     if not args.no_cpu_baseline:
