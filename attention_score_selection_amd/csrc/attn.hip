@@ -299,8 +299,16 @@ template <int DT, int D, int NG, bool ORD>
 __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
   using G = Geom<DT, D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::TILE];
-  // LSE of the job's rows (a row chunk holds at most kChunkRows rows), in
-  // log2 units, padded to whole tiles with +inf.
+  // Per row of the job (a row chunk holds at most kChunkRows rows) the value
+  // its scores start from, padded to whole tiles with rows that contribute 0:
+  // with SEED, -LSE / scale, the initial value of the MFMA accumulation
+  // chains, so that the epilogue is exp2(c1 * acc) and the LSE registers die
+  // at the tile's first MFMAs (padding -inf); otherwise LSE * log2(e),
+  // subtracted in the epilogue, exp2(c1 * acc - lse2) (padding +inf).  The
+  // seeded form frees the registers a fourth resident key group needs at
+  // d = 96..128 with 16-bit inputs; fp8 holds four groups either way and
+  // measured 1% faster unseeded.
+  constexpr bool SEED = DT != TSEL_FP8_E4M3;
   __shared__ __attribute__((aligned(16))) float slse[kChunkRows + kRows];
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
@@ -389,6 +397,7 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     const int nr = ntiles * kRows;
     const int dmax = chunk_hi - 1 - row_lo;   // last token offset of the chunk
     const int lf = 31 - __builtin_clz(F);     // F is a power of two
+    const float inv_c1 = 1.0f / a.c1;
     // Batches of eight independent loads per thread (token offsets clamped
     // into the chunk, so every address is valid), then the stores.
     for (int r0 = 0; r0 < nr; r0 += 256 * 8) {
@@ -401,7 +410,8 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = r0 + 256 * u + (int)threadIdx.x;
-        if (r < nr) slse[r] = (r >> lf) <= dmax ? v[u] * 1.44269504088896340736f : kPosInf;
+        const float l2 = v[u] * 1.44269504088896340736f;
+        if (r < nr) slse[r] = (r >> lf) <= dmax ? (SEED ? -l2 * inv_c1 : l2) : (SEED ? kNegInf : kPosInf);
       }
     }
   }
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     float l2[16];
     if (MODE != 0) {
       read_frag<DT, D>(af, b);
-      // LSE of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3.
+      // Start values (or LSE) of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3.
       const float *lb = slse + it * kRows + 4 * (lane >> 5);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -456,7 +466,14 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     if (it + 1 < ntiles) load(it + 1);
     if (MODE != 0) {
       f32x16 s[NG];
-      tile_mma<DT, D, NG>(af, kf, s);
+      if constexpr (SEED) {
+        f32x16 seed;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) seed[v] = l2[v];
+        tile_mma_seeded<DT, D, NG>(af, kf, s, seed);
+      } else {
+        tile_mma<DT, D, NG>(af, kf, s);
+      }
       const int tt0 = row_lo + it * tpt;
       auto epi = [&](int n, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
@@ -467,7 +484,7 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
         float p[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          p[v] = fast_exp2(fmaf(s[n][v], a.c1, -l2[v]));
+          p[v] = fast_exp2(SEED ? s[n][v] * a.c1 : fmaf(s[n][v], a.c1, -l2[v]));
           if (MASKED) p[v] = (acc_row_c(v) >= thr) ? p[v] : 0.0f;
         }
         cs[n] += tree16(p);

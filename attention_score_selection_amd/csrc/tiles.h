@@ -305,6 +305,20 @@ __device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[kch(DT, D)],
   }
 }
 
+// The same with every accumulation chain starting from `seed` instead of 0.
+template <int DT, int D, int NG>
+__device__ __forceinline__ void tile_mma_seeded(const Chunk<DT> (&af)[kch(DT, D)],
+                                                const Chunk<DT> (&res)[NG][kch(DT, D)],
+                                                f32x16 (&acc)[NG], const f32x16 &seed) {
+#pragma unroll
+  for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[0], res[n][0], seed);
+#pragma unroll
+  for (int kc = 1; kc < kch(DT, D); ++kc) {
+#pragma unroll
+    for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[kc], res[n][kc], acc[n]);
+  }
+}
+
 // Row of the 32x32 accumulator held in register v by this lane is
 // acc_row_c(v) + 4 * (lane / 32); acc_row_c is a compile-time constant, so a
 // mask test against a per-lane threshold costs one compare per register.
