@@ -17,8 +17,9 @@
 //  * Column score (attention a vision token receives: LiteVLM review,
 //    formula section; a column-wise reduction that never materialises the
 //    attention matrix: REDtech article, section 3.2): resident = candidate
-//    keys, streamed = query-row tiles with their LSE.  Columns reduce in-lane;
-//    nothing of P leaves the registers.
+//    keys, streamed = query-row tiles; each tile's accumulation chains start
+//    from its rows' -LSE/scale, held in LDS for the job.  Columns reduce
+//    in-lane; nothing of P leaves the registers.
 //
 // Query heads that share a KV head are folded into the row dimension (F heads
 // per token in each 32-row group), so one key fragment serves F query heads.
@@ -292,8 +293,8 @@ __global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
 // Column-score kernel.
 // Job = (head block hb, segment a, row chunk rc, key block kb).  Each wave
 // holds NG*32 candidate keys; query-row tiles of 32 rows (32/F tokens x F
-// heads) and their LSE stream through LDS; per-column partial sums go to
-// partial[(hb*RCmax + rc)*N + c].
+// heads) stream through LDS, the rows' LSE terms are put in LDS once per job;
+// per-column partial sums go to partial[(hb*RCmax + rc)*N + c].
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NG, bool ORD>
 __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
