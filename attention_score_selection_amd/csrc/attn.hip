@@ -454,8 +454,9 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     Chunk<DT> af[G::KCH];
     float l2[16];
     if (MODE != 0) {
-      read_frag<DT, D>(af, b);
-      // Start values (or LSE) of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3.
+      // Start values (or LSE) of this lane's rows 8q + 4*(lane/32) + 0..3,
+      // q = 0..3, read before the fragments: the seeded chains need them at
+      // their first MFMA, and LDS reads return in order.
       const float *lb = slse + it * kRows + 4 * (lane >> 5);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -463,6 +464,7 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
 #pragma unroll
         for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
       }
+      read_frag<DT, D>(af, b);
     }
     if (it + 1 < ntiles) load(it + 1);
     if (MODE != 0) {
