@@ -455,16 +455,21 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     float l2[16];
     if (MODE != 0) {
       // Start values (or LSE) of this lane's rows 8q + 4*(lane/32) + 0..3,
-      // q = 0..3, read before the fragments: the seeded chains need them at
-      // their first MFMA, and LDS reads return in order.
-      const float *lb = slse + it * kRows + 4 * (lane >> 5);
+      // q = 0..3.  With SEED they are read before the fragments: the chains
+      // need them at their first MFMA, and LDS reads return in order; the
+      // LSE form is needed only by the epilogue, after the fragments.
+      auto read_rows = [&]() {
+        const float *lb = slse + it * kRows + 4 * (lane >> 5);
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
-      }
+          for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
+        }
+      };
+      if (SEED) read_rows();
       read_frag<DT, D>(af, b);
+      if (!SEED) read_rows();
     }
     if (it + 1 < ntiles) load(it + 1);
     if (MODE != 0) {
