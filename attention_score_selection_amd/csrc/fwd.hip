@@ -121,7 +121,7 @@ __device__ __forceinline__ Chunk<DT> read_vt(const char *vt, int dg, int c) {
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs fa) {
+__global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   using G = Geom<DT, D>;
   using VG = VGeom<DT, D>;
   constexpr int BUF = G::TILE + VG::BYTES;
@@ -212,9 +212,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs fa) {
   store(0);
   if (1 < ntiles) load(1);
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = key_lo + kRows * it;
-    if (!(a.causal && k0 > wtok_max)) {  // otherwise no row of this wave sees the tile
+  // Tiles in three runs for this wave: keys every row of the wave sees, keys
+  // near its rows (masked per lane: past the segment end or, causal, past
+  // the row's token), keys after its last row (causal; skipped, still staged).
+  auto tiles_upto = [&](int last_key) {  // tiles whose keys all lie at or before last_key
+    const int x = last_key - key_lo - (kRows - 1);
+    return x < 0 ? 0 : min(ntiles, x / kRows + 1);
+  };
+  auto tiles_from = [&](int last_key) {  // tiles whose first key lies at or before last_key
+    const int x = last_key - key_lo;
+    return x < 0 ? 0 : min(ntiles, x / kRows + 1);
+  };
+  const int full_end = uni(tiles_upto(a.causal ? min(key_hi - 1, wtok0) : key_hi - 1));
+  const int seen_end = uni(a.causal ? tiles_from(wtok_max) : ntiles);
+
+  auto step = [&](int it, auto mode) {
+    constexpr int MODE = decltype(mode)::value;  // 0: skipped, 1: masked, 2: every key visible
+    if (MODE != 0) {
+      const int k0 = key_lo + kRows * it;
       const char *b = buf(it);
       Chunk<DT> af[G::KCH];
       read_frag<DT, D>(af, b);
@@ -223,12 +238,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs fa) {
       // Log2-scaled logits; invisible keys (past the segment end, or later
       // than the row's token under the causal mask) become -inf.
       float x[16];
-      const bool masked = (k0 + kRows > key_hi) || (a.causal && k0 + kRows - 1 > wtok0);
-      const int lim = min(key_hi - 1, a.causal ? qtok : key_hi - 1) - (k0 + 4 * (lane >> 5));
+      const int lim = MODE == 1 ? min(key_hi - 1, a.causal ? qtok : key_hi - 1) - (k0 + 4 * (lane >> 5)) : 0;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         x[v] = s[0][v] * a.c1;
-        if (masked) x[v] = (acc_row_c(v) <= lim) ? x[v] : kNegInf;
+        if (MODE == 1) x[v] = (acc_row_c(v) <= lim) ? x[v] : kNegInf;
       }
       float tmax = x[0];
 #pragma unroll
@@ -262,7 +276,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs fa) {
       if (it + 2 < ntiles) load(it + 2);
     }
     __syncthreads();
-  }
+  };
+  int it = 0;
+  for (; it < full_end; ++it) step(it, std::integral_constant<int, 2>{});
+  for (; it < seen_end; ++it) step(it, std::integral_constant<int, 1>{});
+  for (; it < ntiles; ++it) step(it, std::integral_constant<int, 0>{});
 
   // Both lane halves hold the same rows over different keys: combine the sums.
   const float lt = l + __shfl_xor(l, 32, 64);
