@@ -235,19 +235,21 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
       read_frag<DT, D>(af, b);
       f32x16 s[1];
       tile_mma<DT, D, 1>(af, qf, s);
-      // Log2-scaled logits; invisible keys (past the segment end, or later
-      // than the row's token under the causal mask) become -inf.
+      // Raw logits; invisible keys (past the segment end, or later than the
+      // row's token under the causal mask) become -inf.  c1 > 0, so the
+      // tile's log2-scaled maximum is c1 times the raw one, and each
+      // probability is exp2(fma(s, c1, -m)).
       float x[16];
       const int lim = MODE == 1 ? min(key_hi - 1, a.causal ? qtok : key_hi - 1) - (k0 + 4 * (lane >> 5)) : 0;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        x[v] = s[0][v] * a.c1;
+        x[v] = s[0][v];
         if (MODE == 1) x[v] = (acc_row_c(v) <= lim) ? x[v] : kNegInf;
       }
       float tmax = x[0];
 #pragma unroll
       for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, x[v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * a.c1;
       const bool move = tmax > m + kRescale;
       if (__ballot(move)) {
         const float m_new = move ? tmax : m;
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
       }
       float p[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(x[v] - m);
+      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(x[v], a.c1, -m));
       l += tree16(p);
       const Chunk<DT> p0 = pack_p<DT>(p, 0), p1 = pack_p<DT>(p, 1);
       const char *vt = b + G::TILE;
