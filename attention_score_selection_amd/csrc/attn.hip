@@ -44,13 +44,14 @@ namespace tsel {
 // them (masked per lane), tiles from seen_end on to none (skipped; the wave
 // still stages them and joins every barrier).  MAXMODE: acc = running max of
 // the raw logit over this lane's keys.  Otherwise acc = running sum of
-// exp2(c1*s - m) over this lane's keys.
-template <int DT, int D, int NG, bool MAXMODE>
+// exp2(c1*s - m) over this lane's keys; with FIRSTM, m is first set from
+// tile 0 (its row max in log2 units plus 32) before that tile's terms.
+template <int DT, int D, int NG, bool MAXMODE, bool FIRSTM = false>
 __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageDirect<DT, D> &st,
                                          const char *kbase, int tile_bytes, int key_lo, int key_hi, int nt,
                                          int full_end, int seen_end,
                                          const Chunk<DT> (&qf)[NG][kch(DT, D)],
-                                         const int (&qtok)[NG], const float (&m)[NG],
+                                         const int (&qtok)[NG], float (&m)[NG],
                                          float (&acc)[NG]) {
   using G = Geom<DT, D>;
 #pragma unroll
@@ -67,12 +68,18 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageDir
   load(0);
   __syncthreads();
 
-  // One tile (MODE 0: skipped, 1: masked, 2: visible to every row).
-  auto step = [&](int it, auto mode) {
+  // One tile (MODE 0: skipped, 1: masked, 2: visible to every row; FIRST:
+  // tile 0 of a FIRSTM pass).
+  auto step = [&](int it, auto mode, auto first) {
     constexpr int MODE = decltype(mode)::value;
+    constexpr bool FIRST = decltype(first)::value;
     Chunk<DT> af[G::KCH];
     if (MODE != 0) read_frag<DT, D>(af, smem + (it & 1) * G::TILE);
     if (it + 1 < nt) load(it + 1);
+    if (FIRST && MODE == 0) {
+#pragma unroll
+      for (int n = 0; n < NG; ++n) m[n] = kNegInf;  // no row of this wave sees tile 0
+    }
     if (MODE != 0) {
       const int k0 = key_lo + kRows * it;
       f32x16 s[NG];
@@ -84,6 +91,12 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageDir
         const int lim = MODE == 1 ? min(key_hi - 1, a.causal ? qtok[n] : key_hi - 1) -
                                         (k0 + 4 * (lane_id() >> 5))
                                   : 0;
+        if (FIRST) {
+          float t = kNegInf;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) t = fmaxf(t, (MODE == 2 || acc_row_c(v) <= lim) ? s[n][v] : kNegInf);
+          m[n] = fmaxf(t, __shfl_xor(t, 32, 64)) * a.c1 + 32.0f;
+        }
         float p[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -107,9 +120,15 @@ __device__ __forceinline__ void lse_pass(char *smem, const AttnArgs &a, StageDir
     __syncthreads();
   };
   int it = 0;
-  for (; it < full_end; ++it) step(it, std::integral_constant<int, 2>{});
-  for (; it < seen_end; ++it) step(it, std::integral_constant<int, 1>{});
-  for (; it < nt; ++it) step(it, std::integral_constant<int, 0>{});
+  if (FIRSTM && nt > 0) {
+    if (0 < full_end) step(0, std::integral_constant<int, 2>{}, std::true_type{});
+    else if (0 < seen_end) step(0, std::integral_constant<int, 1>{}, std::true_type{});
+    else step(0, std::integral_constant<int, 0>{}, std::true_type{});
+    it = 1;
+  }
+  for (; it < full_end; ++it) step(it, std::integral_constant<int, 2>{}, std::false_type{});
+  for (; it < seen_end; ++it) step(it, std::integral_constant<int, 1>{}, std::false_type{});
+  for (; it < nt; ++it) step(it, std::integral_constant<int, 0>{}, std::false_type{});
 }
 
 // Kernel argument carrying the job permutation (ORD) or nothing.
@@ -207,18 +226,15 @@ __global__ __launch_bounds__(256, 2) void lse_kernel(AttnArgs a, PermArg<ORD> pa
 
   // Offset m: max logit of the first key tile (which every row sees, except,
   // in a later key split of a causal row block, the rows before the split)
-  // plus 32 (log2 units); the sum pass then cannot overflow unless a later
-  // logit exceeds it by ~100, which the check below catches.
+  // plus 32 (log2 units), taken from that tile inside the sum pass; the sum
+  // then cannot overflow unless a later logit exceeds it by ~100, which the
+  // check below catches.
   float m[NG], acc[NG];
 #pragma unroll
   for (int n = 0; n < NG; ++n) m[n] = 0.f;
   if (threadIdx.x == 0) s_bad = 0;
-  lse_pass<DT, D, NG, true>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, 1, min(full_end, 1), min(seen_end, 1),
-                            qf, qtok, m, acc);
-#pragma unroll
-  for (int n = 0; n < NG; ++n) m[n] = fmaxf(acc[n], __shfl_xor(acc[n], 32, 64)) * a.c1 + 32.0f;
-  lse_pass<DT, D, NG, false>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, ntiles, full_end, seen_end, qf, qtok,
-                             m, acc);
+  lse_pass<DT, D, NG, false, true>(smem, a, st, kbase, tile_bytes, key_lo, key_hi, ntiles, full_end, seen_end, qf,
+                                   qtok, m, acc);
   float tot[NG];
   bool ok = true;
 #pragma unroll
