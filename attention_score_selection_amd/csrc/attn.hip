@@ -313,19 +313,16 @@ __global__ __launch_bounds__(256) void lse_merge(AttnArgs a) {
 // per-column partial sums go to partial[(hb*RCmax + rc)*N + c].
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NG, bool ORD>
-__global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
+__global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArgs a, PermArg<ORD> pa) {
   using G = Geom<DT, D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * G::TILE];
   // Per row of the job (a row chunk holds at most kChunkRows rows) the value
-  // its scores start from, padded to whole tiles with rows that contribute 0:
-  // with SEED, -LSE / scale, the initial value of the MFMA accumulation
-  // chains, so that the epilogue is exp2(c1 * acc) and the LSE registers die
-  // at the tile's first MFMAs (padding -inf); otherwise LSE * log2(e),
-  // subtracted in the epilogue, exp2(c1 * acc - lse2) (padding +inf).  The
-  // seeded form frees the registers a fourth resident key group needs at
-  // d = 96..128 with 16-bit inputs; fp8 holds four groups either way and
-  // measured 1% faster unseeded.
-  constexpr bool SEED = DT != TSEL_FP8_E4M3;
+  // its scores start from, -LSE / scale, padded to whole tiles with -inf
+  // (rows that contribute 0): the initial value of the MFMA accumulation
+  // chains, so that the epilogue is exp2(c1 * acc) and no LSE registers live
+  // through it.  That frees the registers a fourth resident key group needs
+  // at d = 96..128 with 16-bit inputs, and lets fp8 run three workgroups per
+  // CU.
   __shared__ __attribute__((aligned(16))) float slse[kChunkRows + kRows];
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
@@ -427,8 +424,7 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = r0 + 256 * u + (int)threadIdx.x;
-        const float l2 = v[u] * 1.44269504088896340736f;
-        if (r < nr) slse[r] = (r >> lf) <= dmax ? (SEED ? -l2 * inv_c1 : l2) : (SEED ? kNegInf : kPosInf);
+        if (r < nr) slse[r] = (r >> lf) <= dmax ? -(v[u] * 1.44269504088896340736f) * inv_c1 : kNegInf;
       }
     }
   }
@@ -470,34 +466,25 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
     Chunk<DT> af[G::KCH];
     float l2[16];
     if (MODE != 0) {
-      // Start values (or LSE) of this lane's rows 8q + 4*(lane/32) + 0..3,
-      // q = 0..3.  With SEED they are read before the fragments: the chains
-      // need them at their first MFMA, and LDS reads return in order; the
-      // LSE form is needed only by the epilogue, after the fragments.
-      auto read_rows = [&]() {
-        const float *lb = slse + it * kRows + 4 * (lane >> 5);
+      // Start values of this lane's rows 8q + 4*(lane/32) + 0..3, q = 0..3,
+      // read before the fragments: the chains need them at their first
+      // MFMA, and LDS reads return in order.
+      const float *lb = slse + it * kRows + 4 * (lane >> 5);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4v v4 = *reinterpret_cast<const f32x4v *>(lb + 8 * q4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
-        }
-      };
-      if (SEED) read_rows();
+        for (int j = 0; j < 4; ++j) l2[4 * q4 + j] = v4[j];
+      }
       read_frag<DT, D>(af, b);
-      if (!SEED) read_rows();
     }
     if (it + 1 < ntiles) load(it + 1);
     if (MODE != 0) {
       f32x16 s[NG];
-      if constexpr (SEED) {
-        f32x16 seed;
+      f32x16 seed;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) seed[v] = l2[v];
-        tile_mma_seeded<DT, D, NG>(af, kf, s, seed);
-      } else {
-        tile_mma<DT, D, NG>(af, kf, s);
-      }
+      for (int v = 0; v < 16; ++v) seed[v] = l2[v];
+      tile_mma_seeded<DT, D, NG>(af, kf, s, seed);
       const int tt0 = row_lo + it * tpt;
       auto epi = [&](int n, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
@@ -508,7 +495,7 @@ __global__ __launch_bounds__(256, kColWGs) void colscore_kernel(AttnArgs a, Perm
         float p[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          p[v] = fast_exp2(SEED ? s[n][v] * a.c1 : fmaf(s[n][v], a.c1, -l2[v]));
+          p[v] = fast_exp2(s[n][v] * a.c1);
           if (MASKED) p[v] = (acc_row_c(v) >= thr) ? p[v] : 0.0f;
         }
         cs[n] += tree16(p);

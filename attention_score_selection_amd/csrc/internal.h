@@ -218,9 +218,12 @@ constexpr int max_groups(int dtype, int head_dim) {
 // 5% faster on the 16384-token layer and the varlen batch, 9% on the
 // 3214-token one.  Two groups at three workgroups per CU measured the same
 // as three at two on the 16384-token layer and 1% slower on the varlen batch.
+// fp8 (four groups of half the registers) fits three workgroups per CU,
+// where its VALU-bound epilogue gains from the third wave per SIMD: 10%
+// faster on the 16384-token layer.
 constexpr int colscore_groups(int dtype, int head_dim) {
   return max_groups(dtype, head_dim) == 3 && dtype != TSEL_F32 ? 4 : max_groups(dtype, head_dim);
 }
-constexpr int kColWGs = 2;
+constexpr int colscore_wgs(int dtype) { return dtype == TSEL_FP8_E4M3 ? 3 : 2; }
 
 }  // namespace tsel
