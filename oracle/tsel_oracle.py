@@ -136,7 +136,8 @@ def _segment_head(q64, k64, seg, h, g, scale, causal, lse_given):
         S = scale * (Qs[r0:r1] @ Ks[:kend].T)
         if causal:
             rows = np.arange(r0, r1)[:, None]
-            S = np.where(np.arange(kend)[None, :] <= rows, S, -np.inf)
+            seen = np.arange(kend)[None, :] <= rows
+            S = np.where(seen, S, -np.inf)
         if lse_given is None:
             m = S.max(axis=1)
             lse_rows = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
@@ -145,7 +146,12 @@ def _segment_head(q64, k64, seg, h, g, scale, causal, lse_given):
         lse_out[r0:r1] = lse_rows
         vis = loc < kend
         if vis.any():
-            P = np.exp(S[:, loc[vis]] - lse_rows[:, None])
+            with np.errstate(invalid="ignore"):  # -inf - (-inf) at masked pairs, zeroed below
+                P = np.exp(S[:, loc[vis]] - lse_rows[:, None])
+            if causal:
+                # A masked pair adds nothing to the mass, whatever the row's
+                # (supplied) LSE: exp(-inf - LSE) is 0 for every LSE but -inf.
+                P = np.where(seen[:, loc[vis]], P, 0.0)
             mass[vis] += P.sum(axis=0)
     return lse_out, mass
 

@@ -505,6 +505,31 @@ def test_supplied_lse_identity_and_shift():
     np.testing.assert_allclose(mass_shift, mass * math.exp(-delta), rtol=1e-13)
 
 
+def test_supplied_lse_nonfinite_row_reaches_only_visible_pairs():
+    """A supplied LSE of -inf for one row makes every mass that row reaches
+    +inf and leaves the masses of the candidates it cannot see (causal: later
+    tokens, or other requests) exactly as with that row contributing nothing
+    (LSE = +inf): masked pairs add zero whatever the row's LSE."""
+    p = random_small(15, "causal", dtype="f32", n_req=2)
+    lse, _ = oracle.attention_stats(p)
+    b = 0
+    lo, hi = int(p.cu_seqlens[b]), int(p.cu_seqlens[b + 1])
+    t = lo + (hi - lo) // 2
+    h = 1 % p.hq
+    neg, pos = lse.copy(), lse.copy()
+    neg[h, t], pos[h, t] = -np.inf, np.inf
+    _, m_neg = oracle.attention_stats(p, lse_in=neg)
+    _, m_pos = oracle.attention_stats(p, lse_in=pos)
+    # token of every candidate
+    tok = np.concatenate([np.arange(p.img_start[s], p.img_start[s] + p.img_hw[s, 0] * p.img_hw[s, 1])
+                          for s in range(p.S)])
+    seen = (tok <= t) & (tok >= lo)
+    assert seen.any() and (~seen).any()
+    assert np.all(np.isposinf(m_neg[seen]))
+    np.testing.assert_array_equal(m_neg[~seen], m_pos[~seen])
+    assert np.all(np.isfinite(m_pos))
+
+
 def test_lse_and_softmax_match_library_routines():
     """Full mask, one request: the LSE is scipy's logsumexp of the logits and
     the mass is the column sum of torch's float64 softmax."""
