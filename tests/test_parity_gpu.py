@@ -542,6 +542,35 @@ def test_supplied_lse_shift_identity(dev):
     assert np.allclose(ratio, np.exp(-0.75), rtol=1e-5)
 
 
+def test_supplied_lse_nonfinite_rows(dev):
+    """A supplied LSE holding +inf (the row contributes nothing), -inf (every
+    score the row reaches becomes +inf) and NaN rows: the column score starts
+    its accumulation chains from -LSE/scale, so these reach the chains
+    directly; scores, their non-finite pattern and the kept sets against the
+    oracle with the same LSE."""
+    prob = random_medium(39, "causal", dtype="f16", hq=4, hkv=2, d=128, n_req=2)
+    announce(prob)
+    lse64, _ = oracle.attention_stats(prob)
+    lse32 = lse64.astype(np.float32)
+    rng = np.random.default_rng(39)
+    t0, t1 = int(prob.cu_seqlens[1]), int(prob.cu_seqlens[2])
+    for val in (np.inf, -np.inf, np.nan):
+        h = int(rng.integers(0, prob.hq))
+        t = int(rng.integers(t0 + (t1 - t0) // 2, t1))  # a late row of request 1
+        lse32[h, t] = val
+    ref = oracle.run(prob, lse_in=lse32.astype(np.float64), with_emb=False)
+    got = P.run_gpu(prob, dev, lse=lse32)
+    assert np.array_equal(np.isnan(got["score"]), np.isnan(ref["score"]))
+    assert np.array_equal(np.isposinf(got["score"]), np.isposinf(ref["score"]))
+    assert np.isnan(ref["score"]).any() and np.isposinf(ref["score"]).any()
+    fin = np.isfinite(ref["score"])
+    rtol = P.rtol_of(prob)
+    assert np.all(np.abs(got["score"][fin] - ref["score"][fin]) <=
+                  np.maximum(rtol * np.abs(ref["score"][fin]), 1e-6))
+    assert np.array_equal(got["k"], ref["k"])
+    P.check_keep(prob, got["keep"], np.where(np.isfinite(ref["mass"]), ref["mass"], -np.inf), ref["k"])
+
+
 def test_deterministic_repeat(dev):
     prob = random_medium(38, "causal", dtype="bf16", hq=16, hkv=4, d=128, n_req=3)
     announce(prob)
