@@ -508,6 +508,33 @@ def test_nonfinite_inputs_rank_last(dev):
     assert np.array_equal(got["keep"], ref["keep"])
 
 
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_nonfinite_key_poisons_the_rows_that_see_it(dev, bad):
+    """A NaN or +inf in one key of one KV head: every row of that head group
+    that sees the key has a NaN LSE (for +inf: the logit is +-inf and the
+    row's normaliser inf - inf), and the scores those rows reach are NaN; the
+    same pattern, the remaining scores and the kept sets as the oracle."""
+    prob = random_small(41, "causal", dtype="bf16", hq=4, hkv=2, d=64, n_req=2)
+    k = prob.k.clone()
+    t_bad = int(prob.cu_seqlens[1]) + 5  # an early token of request 1
+    k[t_bad, 1, 7] = bad
+    prob.k = k
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    ref = oracle.run(prob, with_emb=False)
+    assert np.array_equal(np.isnan(got["lse"]), np.isnan(ref["lse"]))
+    assert np.isnan(ref["lse"]).any()
+    fin_l = np.isfinite(ref["lse"])
+    assert np.max(np.abs(got["lse"][fin_l] - ref["lse"][fin_l])) <= P.lse_tol_of(prob)
+    assert np.array_equal(np.isnan(got["score"]), np.isnan(ref["score"]))
+    fin = np.isfinite(ref["score"])
+    rtol = P.rtol_of(prob)
+    assert np.all(np.abs(got["score"][fin] - ref["score"][fin]) <=
+                  np.maximum(rtol * np.abs(ref["score"][fin]), 1e-6))
+    assert np.array_equal(got["k"], ref["k"])
+    P.check_keep(prob, got["keep"], ref["mass"], ref["k"])
+
+
 def test_strided_qk_from_fused_projection(dev):
     """Q and K as views into one fused [T, Hq + 2*Hkv, d] projection."""
     prob = random_medium(36, "causal", dtype="bf16", hq=8, hkv=2, d=128, n_req=2)
