@@ -248,10 +248,10 @@ def main():
                     help="after timing, run kernels of known traffic once each (device copies of 16, "
                          "64, 256 and 1024 MiB, a 1 GiB read-only sum, a 1 GiB fill), to check how "
                          "the HBM byte counters relate to real traffic")
-    ap.add_argument("--calib-gemm", type=int, default=0,
-                    help="also time a plain n x n x n bf16 matrix product (torch.matmul, i.e. the "
-                         "vendor GEMM library) on random data: the MFMA rate a dense library "
-                         "kernel sustains on this GPU")
+    ap.add_argument("--calib-gemm", type=int, default=8192,
+                    help="after timing, also time a plain n x n x n bf16 matrix product (torch.matmul, "
+                         "i.e. the vendor GEMM library) on random data: the MFMA rate a dense library "
+                         "kernel sustains on this GPU, for comparison with the kernels' (0: skip)")
     ap.add_argument("--forward", action="store_true",
                     help="also time the attention forward (tsel_attention_fwd) on the same layer")
     ap.add_argument("--cold", action="store_true",
@@ -437,7 +437,13 @@ def main():
     if args.calib_suite:
         result["calib_suite"] = calib_suite(dev)
     if args.calib_gemm > 0:
-        result["calib_gemm"] = time_gemm(args.calib_gemm, dev, stream, args)
+        gm = time_gemm(args.calib_gemm, dev, stream, args)
+        # The path's kernels against the library GEMM on the same GPU and run
+        # (bf16 products on both sides only when the workload is bf16/f16).
+        if prob.dtype in ("bf16", "f16"):
+            gm["colscore_rate_vs_gemm"] = col_flops / t_col / 1e12 / gm["tflops"]
+            gm["lse_rate_vs_gemm"] = None if prob.lse_supplied else lse_flops / t_lse / 1e12 / gm["tflops"]
+        result["calib_gemm"] = gm
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(prob, col_elems / prob.hq)
     print(json.dumps(result), flush=True)
