@@ -370,29 +370,34 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
   const int F = a.F;
   const int h0 = hb * F;
   const int g = h0 / a.hg;
-  const int wc0 = kb0 + w * NG * kRows;
-  const int wlast = min(wc0 + NG * kRows, kb1) - 1;
-  // Smallest and largest key token of this wave (candidates are in token order).
-  const int wkmax = (wlast >= wc0) ? tok_u(wlast) : -1;
-  const int wkmin = (wlast >= wc0) ? tok_u(wc0) : 0x7fffffff;
-
-  // Resident keys: group n, lane column lane % 32 is candidate wc0 + 32n + lane % 32.
+  // Resident keys: group n of wave w holds the 32 candidates from
+  // gbase(n) = kb0 + 32*(4n + w), lane column lane % 32.  Interleaving the
+  // groups across the four waves splits the groups that a tile near the
+  // causal diagonal reaches evenly between the waves (with contiguous
+  // ranges the first wave would compute them all while the others wait at
+  // the tile's barrier), and a tile computes only the groups it reaches.
+  auto gbase = [&](int n) { return kb0 + kRows * (4 * n + w); };
   Chunk<DT> kf[NG][G::KCH];
   int ktok[NG];
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
-    const int c = wc0 + n * kRows + (lane & 31);
+    const int c = gbase(n) + (lane & 31);
     const int t = few ? img_token(im, min(c, kb1 - 1)) : cand_token(a.L, s_lo, s_hi, min(c, kb1 - 1));
     ktok[n] = (c < kb1) ? t : 0x7fffffff;
   }
-  // Largest key token of each group (its last candidate before kb1; INT_MAX
-  // marks an empty group, which then always takes the masked path).
-  int gkmax[NG];
+  // First and last key token of each group; the groups holding candidates
+  // are the first nvalid (candidates are in token order), and so are the
+  // groups a tile reaches.
+  int gkmin[NG], gkmax[NG];
+  int nvalid = 0;
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
-    const int last = min(kRows - 1, kb1 - 1 - (wc0 + n * kRows));
+    const int last = min(kRows - 1, kb1 - 1 - gbase(n));
+    gkmin[n] = last >= 0 ? uni(__shfl(ktok[n], 0, 64)) : 0x7fffffff;
     gkmax[n] = last >= 0 ? uni(__shfl(ktok[n], last, 64)) : 0x7fffffff;
+    nvalid += last >= 0 ? 1 : 0;
   }
+  nvalid = uni(nvalid);
   const char *kbase = reinterpret_cast<const char *>(a.k);
   load_resident<DT, D, NG>(kf, [&](int j) -> const char * {
     const int t = ktok[j / kRows];
@@ -450,18 +455,24 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
   load(0);
   __syncthreads();
 
-  // Tiles in three runs for this wave (causal): every row before every key
-  // (skipped), rows that reach some key of the wave (masked where a group's
-  // last key is later than the tile's first row), then rows past all its
-  // keys.  Every wave runs every tile's barrier and load.
-  const int skip_end = a.causal ? uni(min(ntiles, max(0, (wkmin - row_lo) / tpt))) : 0;
-  const int full_start =
-      a.causal ? uni(min(ntiles, max(skip_end, (wkmax - row_lo + tpt - 1) / tpt))) : 0;
+  // Runs of tiles for this wave (causal): rows before every key (skipped);
+  // rows that reach the first m groups, m = 1..nvalid (masked where a
+  // group's last key is later than the tile's first row); then rows past
+  // all its keys (unmasked).  Tile it reaches group n from live(n) on.
+  // Every wave runs every tile's barrier and load.
+  auto live = [&](int n) {
+    return n < nvalid ? (a.causal ? uni(min(ntiles, max(0, (gkmin[n] - row_lo) / tpt))) : 0) : ntiles;
+  };
+  const int full_start = uni(
+      nvalid == 0 ? ntiles
+                  : (a.causal ? min(ntiles, max(live(nvalid - 1), (gkmax[nvalid - 1] - row_lo + tpt - 1) / tpt)) : 0));
 
   // One tile: refill the other buffer (read last step), then the MFMAs and
-  // the epilogue of this tile (MODE 0: skipped, 1: masked, 2: unmasked).
-  auto step = [&](int it, auto mode) {
+  // the epilogue of this tile for the first M groups (MODE 0: skipped,
+  // 1: masked where needed, 2: unmasked).
+  auto step = [&](int it, auto mode, auto groups) {
     constexpr int MODE = decltype(mode)::value;
+    constexpr int M = decltype(groups)::value;
     const char *b = buf(it);
     Chunk<DT> af[G::KCH];
     float l2[16];
@@ -484,7 +495,7 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
       f32x16 seed;
 #pragma unroll
       for (int v = 0; v < 16; ++v) seed[v] = l2[v];
-      tile_mma_seeded<DT, D, NG>(af, kf, s, seed);
+      tile_mma_seeded<DT, D, NG, M>(af, kf, s, seed);
       const int tt0 = row_lo + it * tpt;
       auto epi = [&](int n, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
@@ -502,12 +513,12 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
       };
       if (MODE == 2) {
 #pragma unroll
-        for (int n = 0; n < NG; ++n) epi(n, std::false_type{});
+        for (int n = 0; n < M; ++n) epi(n, std::false_type{});
       } else {
         // Near the diagonal only the groups whose last key is later than the
         // tile's first token need the mask.
 #pragma unroll
-        for (int n = 0; n < NG; ++n) {
+        for (int n = 0; n < M; ++n) {
           if (tt0 < gkmax[n]) epi(n, std::true_type{});
           else epi(n, std::false_type{});
         }
@@ -519,16 +530,44 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
+  using Skip = std::integral_constant<int, 0>;
+  using Masked = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<int, 2>;
   int it = 0;
-  for (; it < skip_end; ++it) step(it, std::integral_constant<int, 0>{});
-  for (; it < full_start; ++it) step(it, std::integral_constant<int, 1>{});
-  for (; it < ntiles; ++it) step(it, std::integral_constant<int, 2>{});
+  for (const int e = uni(live(0)); it < e; ++it) step(it, Skip{}, std::integral_constant<int, 1>{});
+  // m groups reached: up to the tile that reaches group m (or, for the last
+  // run, up to the first tile past all keys).
+  auto masked_run = [&](auto groups) {
+    constexpr int M = decltype(groups)::value;
+    if (M > nvalid) return;
+    for (const int e = uni(M < nvalid ? live(M) : full_start); it < e; ++it) step(it, Masked{}, groups);
+  };
+  auto full_run = [&](auto groups) {
+    for (; it < ntiles; ++it) step(it, Full{}, groups);
+  };
+  masked_run(std::integral_constant<int, 1>{});
+  if constexpr (NG >= 2) masked_run(std::integral_constant<int, 2>{});
+  if constexpr (NG >= 3) masked_run(std::integral_constant<int, 3>{});
+  if constexpr (NG >= 4) masked_run(std::integral_constant<int, 4>{});
+  static_assert(NG <= 4, "runs are written out for up to four groups");
+  if (nvalid == NG) full_run(std::integral_constant<int, NG>{});
+  else if constexpr (NG >= 2) {
+    if (nvalid == 1) full_run(std::integral_constant<int, 1>{});
+    else if constexpr (NG >= 3) {
+      if (nvalid == 2) full_run(std::integral_constant<int, 2>{});
+      else if constexpr (NG >= 4) {
+        if (nvalid == 3) full_run(std::integral_constant<int, 3>{});
+      }
+    }
+  }
+  // A wave without candidates (only in a segment's last key block) skips.
+  for (; it < ntiles; ++it) step(it, Skip{}, std::integral_constant<int, 1>{});
 
   float *out = a.partial + ((long long)hb * a.RCmax + rc) * a.N;
 #pragma unroll
   for (int n = 0; n < NG; ++n) {
     const float v = cs[n] + __shfl_xor(cs[n], 32, 64);
-    const int c = wc0 + n * kRows + (lane & 31);
+    const int c = gbase(n) + (lane & 31);
     if (lane < 32 && c < kb1) out[c] = v;
   }
 }

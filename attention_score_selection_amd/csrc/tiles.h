@@ -305,17 +305,19 @@ __device__ __forceinline__ void tile_mma(const Chunk<DT> (&af)[kch(DT, D)],
   }
 }
 
-// The same with every accumulation chain starting from `seed` instead of 0.
-template <int DT, int D, int NG>
+// The same with every accumulation chain starting from `seed` instead of 0,
+// for the first M of the NG resident groups only.
+template <int DT, int D, int NG, int M = NG>
 __device__ __forceinline__ void tile_mma_seeded(const Chunk<DT> (&af)[kch(DT, D)],
                                                 const Chunk<DT> (&res)[NG][kch(DT, D)],
                                                 f32x16 (&acc)[NG], const f32x16 &seed) {
+  static_assert(M >= 1 && M <= NG, "group count");
 #pragma unroll
-  for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[0], res[n][0], seed);
+  for (int n = 0; n < M; ++n) acc[n] = mma<DT>(af[0], res[n][0], seed);
 #pragma unroll
   for (int kc = 1; kc < kch(DT, D); ++kc) {
 #pragma unroll
-    for (int n = 0; n < NG; ++n) acc[n] = mma<DT>(af[kc], res[n][kc], acc[n]);
+    for (int n = 0; n < M; ++n) acc[n] = mma<DT>(af[kc], res[n][kc], acc[n]);
   }
 }
 
