@@ -488,6 +488,33 @@ def test_many_images_in_one_request(dev, n_img):
     P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
 
 
+# Images whose candidate counts leave every kind of last key block: with
+# four resident 32-key groups per wave a key block holds 512 candidates, and
+# a block of 1, 31, 33, 96, 97, 129, 300 or 511 leaves waves with no group,
+# with one partly filled group, or with fewer groups than the others.
+RAGGED_IMAGES = [(27, 19), (1, 31), (5, 109), (1, 97), (3, 43), (19, 32), (31, 33), (28, 29), (1, 1), (7, 73)]
+
+
+@pytest.mark.parametrize("mask,dtype,hq,hkv,d", [("causal", "bf16", 16, 16, 64), ("causal", "f16", 32, 4, 128),
+                                                 ("full", "bf16", 16, 16, 64), ("causal", "fp8", 16, 16, 128)])
+def test_ragged_key_block_tails(dev, mask, dtype, hq, hkv, d):
+    """One image per request, each a different candidate count; text before
+    and after it.  Sized so that the column score keeps its widest key
+    blocks (at least 512 jobs once row chunks are cut to 64 tokens); every
+    score, kept set and compaction against the oracle."""
+    reqs = [(7 + h * w + 40, [(7, h, w)]) for h, w in RAGGED_IMAGES]
+    F = 1
+    while F < 16 and (hq // hkv) % (2 * F) == 0:
+        F *= 2
+    jobs_at_64 = (hq // F) * sum(((h * w + 511) // 512) * ((n + 63) // 64) for n, ((_, h, w),) in reqs)
+    assert jobs_at_64 >= 512, jobs_at_64
+    prob = make_problem(f"ragged_tails_{mask}_{dtype}_{hq}x{hkv}_d{d}", reqs, hq, hkv, d, dtype, mask,
+                        1.0, 400 + d + hq, ratio_range=(0.3, 0.8), emb_dim=16)
+    announce(prob)
+    got = P.run_gpu(prob, dev)
+    P.full_check(prob, got, oracle.run(prob, with_emb=False), prob.emb)
+
+
 def test_nonfinite_inputs_rank_last(dev):
     """A NaN in one query row poisons the LSE of that row and the scores of
     every candidate the row sees; those rank as -inf, identically on both sides."""
