@@ -324,6 +324,10 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
   // at d = 96..128 with 16-bit inputs, and lets fp8 run three workgroups per
   // CU.
   __shared__ __attribute__((aligned(16))) float slse[kChunkRows + kRows];
+  // Key token of each lane column of each resident group, per wave: read by
+  // the masked tiles near the causal diagonal, which run after the unmasked
+  // ones, so these values are not held in registers through the main loop.
+  __shared__ int sktok[4][NG][kRows];
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
   if (job >= a.total_jobs) return;
@@ -452,7 +456,9 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
     if (it + 1 < ntiles) st.template load_at<false>(buf(it), qrs, it * tile_step, kRows);
     else st.template load_at<true>(buf(it), qrs, it * tile_step, last_rows);
   };
-  load(0);
+#pragma unroll
+  for (int n = 0; n < NG; ++n) sktok[w][n][lane & 31] = ktok[n];
+  load(ntiles - 1);
   __syncthreads();
 
   // Runs of tiles for this wave (causal): rows before every key (skipped);
@@ -467,9 +473,9 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
       nvalid == 0 ? ntiles
                   : (a.causal ? min(ntiles, max(live(nvalid - 1), (gkmax[nvalid - 1] - row_lo + tpt - 1) / tpt)) : 0));
 
-  // One tile: refill the other buffer (read last step), then the MFMAs and
-  // the epilogue of this tile for the first M groups (MODE 0: skipped,
-  // 1: masked where needed, 2: unmasked).
+  // One tile: start loading the next one (tile it - 1) into the other buffer
+  // (read last step), then the MFMAs and the epilogue of this tile for the
+  // first M groups (MODE 0: skipped, 1: masked where needed, 2: unmasked).
   auto step = [&](int it, auto mode, auto groups) {
     constexpr int MODE = decltype(mode)::value;
     constexpr int M = decltype(groups)::value;
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
       }
       read_frag<DT, D>(af, b);
     }
-    if (it + 1 < ntiles) load(it + 1);
+    if (it > 0) load(it - 1);
     if (MODE != 0) {
       f32x16 s[NG];
       f32x16 seed;
@@ -500,9 +506,9 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
       auto epi = [&](int n, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         // Row of register v has token tt0 + (acc_row_c(v) + 4*(lane/32)) / F;
-        // it sees key token ktok[n] iff acc_row_c(v) >= (ktok[n] - tt0)*F -
-        // 4*(lane/32) (the clamp keeps past-the-end columns invisible).
-        const int thr = MASKED ? min(ktok[n] - tt0, kRows) * F - 4 * (lane >> 5) : 0;
+        // it sees key token kt iff acc_row_c(v) >= (kt - tt0)*F - 4*(lane/32)
+        // (the clamp keeps past-the-end columns invisible).
+        const int thr = MASKED ? min(sktok[w][n][lane & 31] - tt0, kRows) * F - 4 * (lane >> 5) : 0;
         float p[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -533,23 +539,16 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
   using Skip = std::integral_constant<int, 0>;
   using Masked = std::integral_constant<int, 1>;
   using Full = std::integral_constant<int, 2>;
-  int it = 0;
-  for (const int e = uni(live(0)); it < e; ++it) step(it, Skip{}, std::integral_constant<int, 1>{});
-  // m groups reached: up to the tile that reaches group m (or, for the last
-  // run, up to the first tile past all keys).
-  auto masked_run = [&](auto groups) {
-    constexpr int M = decltype(groups)::value;
-    if (M > nvalid) return;
-    for (const int e = uni(M < nvalid ? live(M) : full_start); it < e; ++it) step(it, Masked{}, groups);
-  };
+  // The tiles run from the last one down: every job of a row chunk then
+  // starts on the chunk's last tile whatever its key block, so the jobs of
+  // one chunk that run at the same time read the same query tiles in step
+  // (one fetch into L2 serves them all).  First the tiles past all of this
+  // wave's keys, then those reaching its first m groups, m = nvalid .. 1,
+  // then the tiles before its first key.
+  int it = ntiles - 1;
   auto full_run = [&](auto groups) {
-    for (; it < ntiles; ++it) step(it, Full{}, groups);
+    for (; it >= full_start; --it) step(it, Full{}, groups);
   };
-  masked_run(std::integral_constant<int, 1>{});
-  if constexpr (NG >= 2) masked_run(std::integral_constant<int, 2>{});
-  if constexpr (NG >= 3) masked_run(std::integral_constant<int, 3>{});
-  if constexpr (NG >= 4) masked_run(std::integral_constant<int, 4>{});
-  static_assert(NG <= 4, "runs are written out for up to four groups");
   if (nvalid == NG) full_run(std::integral_constant<int, NG>{});
   else if constexpr (NG >= 2) {
     if (nvalid == 1) full_run(std::integral_constant<int, 1>{});
@@ -560,8 +559,20 @@ __global__ __launch_bounds__(256, colscore_wgs(DT)) void colscore_kernel(AttnArg
       }
     }
   }
-  // A wave without candidates (only in a segment's last key block) skips.
-  for (; it < ntiles; ++it) step(it, Skip{}, std::integral_constant<int, 1>{});
+  // m groups reached: down to the first tile that reaches group m.
+  auto masked_run = [&](auto groups) {
+    constexpr int M = decltype(groups)::value;
+    if (M > nvalid) return;
+    for (const int e = uni(live(M - 1)); it >= e; --it) step(it, Masked{}, groups);
+  };
+  static_assert(NG <= 4, "runs are written out for up to four groups");
+  if constexpr (NG >= 4) masked_run(std::integral_constant<int, 4>{});
+  if constexpr (NG >= 3) masked_run(std::integral_constant<int, 3>{});
+  if constexpr (NG >= 2) masked_run(std::integral_constant<int, 2>{});
+  masked_run(std::integral_constant<int, 1>{});
+  // Tiles before the wave's first key (all of them for a wave without
+  // candidates, which only a segment's last key block has).
+  for (; it >= 0; --it) step(it, Skip{}, std::integral_constant<int, 1>{});
 
   float *out = a.partial + ((long long)hb * a.RCmax + rc) * a.N;
 #pragma unroll
