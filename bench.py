@@ -240,7 +240,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps before the timed ones (the GPU clock ramps up over the first ~50 ms of a run from idle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB once (counter calibration)")
