@@ -11,11 +11,12 @@
 // 32-key tile: S^T = K_tile . Q^T on v_mfma_f32_32x32x16 (lane = query row,
 // registers = 16 of the 32 keys), an online softmax in log2 units per lane,
 // and O^T += V_tile^T . P^T, where P^T is the B operand straight from the S^T
-// registers (converted to the input type) and V^T comes from an LDS copy of
-// the value tile stored transposed.  The contraction's k slots of lane half h
-// are the keys 16c + {0..3, 8..11} + 4h of chunk c, which is how the S^T
-// accumulator already holds them; the transposed copy stores the keys in that
-// order, so a V^T fragment is one 16-byte LDS read.
+// registers (converted to the input type) and V^T is read from the row-major
+// value tile with gfx950's transposing LDS read (ds_read_b64_tr_b16).  The
+// contraction's k slots of lane half h are the keys 16c + {0..3, 8..11} + 4h
+// of chunk c, which is how the S^T accumulator already holds them; each group
+// of four keys is one transposing read.  Key and value tiles reach LDS through
+// the LDS-direct form of the buffer load, one tile ahead.
 //
 // The running maximum only moves when a tile's maximum exceeds it by more
 // than 2^8 (so P stays below 2^8, safe for f16 operands); the accumulators are
@@ -27,68 +28,6 @@ namespace tsel {
 namespace {
 
 constexpr float kRescale = 8.0f;  // log2 headroom before the running max moves
-
-// Transposed LDS copy of one 32-key value tile: row d (one per value column,
-// padded to whole 32-row groups) holds the 32 keys' values, VS bytes apart.
-// Within each 16-key chunk the keys are stored in the order 0-3, 8-11, 4-7,
-// 12-15, so the eight keys one lane half contracts over (16c + {0..3, 8..11}
-// + 4h) are adjacent: one 16-byte read per fragment.
-__device__ __forceinline__ constexpr int vt_slot(int key) {
-  return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-template <int DT, int D>
-struct VGeom {
-  static constexpr int ES = Elem<DT>::ES;
-  static constexpr int DG = (D + 31) / 32;     // 32-row groups of O^T
-  static constexpr int VS = kRows * ES + 16;   // row stride (bank spread)
-  static constexpr int BYTES = DG * 32 * VS;
-  static constexpr int DB = D / 8;             // 8-value column blocks
-};
-
-// Register staging of a value tile with the transpose: thread t moves key
-// pair t % 16 (keys 2p, 2p+1) times column block t / 16 (8 columns); it
-// writes 8 LDS words, each holding the two keys' values of one column.
-template <int DT, int D>
-struct VStage {
-  using VG = VGeom<DT, D>;
-  uint4 r0, r1;
-  int off0, off1;  // byte offsets of the two 16-byte units from the tile base
-  int key0;        // first key of the pair (tile row)
-  bool active;
-
-  __device__ __forceinline__ void init(long long vrow_bytes) {
-    const int t = threadIdx.x;
-    key0 = 2 * (t & 15);
-    const int db = t >> 4;
-    active = db < VG::DB;
-    off0 = (int)(key0 * vrow_bytes) + db * 8 * VG::ES;
-    off1 = (int)((key0 + 1) * vrow_bytes) + db * 8 * VG::ES;
-  }
-  // Tile rows [0, nvalid) come from `base` (wave-uniform); the rest are zero.
-  __device__ __forceinline__ void load(const char *base, int nvalid) {
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base);
-    r0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       rs, (active && key0 < nvalid) ? off0 : kOOB, 0, 0));
-    r1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       rs, (active && key0 + 1 < nvalid) ? off1 : kOOB, 0, 0));
-  }
-  __device__ __forceinline__ void store(char *vt) const {
-    if (!active) return;
-    const int db = threadIdx.x >> 4;
-    const uint32_t a[4] = {r0.x, r0.y, r0.z, r0.w};
-    const uint32_t b[4] = {r1.x, r1.y, r1.z, r1.w};
-    char *col = vt + (8 * db) * VG::VS + vt_slot(key0) * VG::ES;  // key0 + 1 is the next slot
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // Column 8db + 2i: low halves of a[i] and b[i]; column 8db + 2i + 1:
-      // their high halves.  (Selector bytes 4..7 pick from the first source.)
-      const uint32_t lo = __builtin_amdgcn_perm(b[i], a[i], 0x05040100u);
-      const uint32_t hi = __builtin_amdgcn_perm(b[i], a[i], 0x07060302u);
-      *reinterpret_cast<uint32_t *>(col + (2 * i) * VG::VS) = lo;
-      *reinterpret_cast<uint32_t *>(col + (2 * i + 1) * VG::VS) = hi;
-    }
-  }
-};
 
 template <int DT> struct PackT;
 template <> struct PackT<TSEL_BF16> { typedef __bf16 T; };
@@ -107,24 +46,48 @@ __device__ __forceinline__ Chunk<DT> pack_p(const float (&p)[16], int c) {
   return r;
 }
 
-// V^T fragment of row group dg, key chunk c: lane row dg*32 + lane%32, keys
-// 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (h = lane / 32), stored
-// adjacently at slots 16c + 8h .. +7.
+// Column groups of O^T: 32 output columns each (the last one padded).
+template <int D> struct OGroups { static constexpr int DG = (D + 31) / 32; };
+
+// This lane's byte offset into a row-major value tile for the transposing
+// reads.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group
+// receives value i % 4 of the 8-byte units that lanes i/4 + 4m (m = 0..3) of
+// its group address.  Here lane j of group gr = lane/16 addresses the four
+// values of columns 16*(gr % 2) + 4*(j % 4) .. +3 in key row 4*(gr / 2) + j/4,
+// so lane i receives, for its own column 16*(gr % 2) + i = lane % 32, the
+// values of keys 4*(gr / 2) + 0..3 = 4*(lane / 32) + 0..3: the first four k
+// slots of its lane half.  The next four (keys + 8) are the same read 8 rows
+// further on.
 template <int DT, int D>
-__device__ __forceinline__ Chunk<DT> read_vt(const char *vt, int dg, int c) {
-  using VG = VGeom<DT, D>;
-  const int lane = lane_id();
-  const char *row = vt + (dg * 32 + (lane & 31)) * VG::VS + (16 * c + 8 * (lane >> 5)) * VG::ES;
+__device__ __forceinline__ int vt_lane_offset() {
+  using G = Geom<DT, D>;
+  const int lane = lane_id(), gr = lane >> 4, j = lane & 15;
+  return (4 * (gr >> 1) + (j >> 2)) * G::RS + (16 * (gr & 1) + 4 * (j & 3)) * G::ES;
+}
+
+// V^T fragment of column group dg, key chunk c: lane column dg*32 + lane%32,
+// keys 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (h = lane / 32).  Columns
+// from D on read padding or the next row and only reach O^T rows that are
+// never written out.
+template <int DT, int D>
+__device__ __forceinline__ Chunk<DT> read_vt(const char *vtile, int lane_off, int dg, int c) {
+  using G = Geom<DT, D>;
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  const char *p = vtile + lane_off + 16 * c * G::RS + dg * 32 * G::ES;
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)p);
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p + 8 * G::RS));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   Chunk<DT> r;
-  r.v[0] = *reinterpret_cast<const uint4 *>(row);
+  r.v[0] = make_uint4(a.x, a.y, b.x, b.y);
   return r;
 }
 
 template <int DT, int D>
 __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   using G = Geom<DT, D>;
-  using VG = VGeom<DT, D>;
-  constexpr int BUF = G::TILE + VG::BYTES;
+  constexpr int DG = OGroups<D>::DG;
+  constexpr int BUF = 2 * G::TILE;  // key tile, then value tile
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
   const AttnArgs &a = fa.at;
 
@@ -160,15 +123,6 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   const int key_hi = uni(a.causal ? tok_hi : seg_hi);
   const int ntiles = uni((key_hi - key_lo + kRows - 1) / kRows);
 
-  // Zero the padding rows of both transposed value tiles once (value columns
-  // D .. 32*DG-1 never get data).
-  if (VG::DG * 32 > D) {
-    for (int i = threadIdx.x; i < (VG::DG * 32 - D) * VG::VS / 4; i += 256) {
-      reinterpret_cast<uint32_t *>(smem + G::TILE + D * VG::VS)[i] = 0u;
-      reinterpret_cast<uint32_t *>(smem + BUF + G::TILE + D * VG::VS)[i] = 0u;
-    }
-  }
-
   // Resident queries: row r of this wave is (token wtok0 + r / F, head h0 + r % F).
   Chunk<DT> qf[1][G::KCH];
   const char *qbase = reinterpret_cast<const char *>(a.q);
@@ -185,32 +139,35 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   const long long krow = a.k_st * G::ES;
   const char *vbase = reinterpret_cast<const char *>(fa.v) + (long long)g * fa.v_sh * G::ES;
   const long long vrow = fa.v_st * G::ES;
-  auto rows_of = [&](int it) { return key_hi - (key_lo + kRows * it); };
-  StageRegs<DT, D> sk;
+  StageDirect<DT, D> sk, sv;
   sk.init([&](int r) { return r * (int)krow; });
-  VStage<DT, D> sv;
-  sv.init(vrow);
+  sv.init([&](int r) { return r * (int)vrow; });
+  const int vt_off = vt_lane_offset<DT, D>();
   auto buf = [&](int it) { return smem + (it & 1) * BUF; };
+  // Start copying key and value tile it into its buffer (one scalar base per
+  // tile; rows past key_hi read as zero).
   auto load = [&](int it) {
     const long long first = key_lo + kRows * it;
-    sk.load(kbase + first * krow, rows_of(it));
-    sv.load(vbase + first * vrow, rows_of(it));
-  };
-  auto store = [&](int it) {
-    sk.store(buf(it));
-    sv.store(buf(it) + G::TILE);
+    const int nv = key_hi - (int)first;
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kbase + first * krow);
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vbase + first * vrow);
+    if (nv >= kRows) {
+      sk.template load_at<false>(buf(it), krs, 0, kRows);
+      sv.template load_at<false>(buf(it) + G::TILE, vrs, 0, kRows);
+    } else {
+      sk.template load_at<true>(buf(it), krs, 0, nv);
+      sv.template load_at<true>(buf(it) + G::TILE, vrs, 0, nv);
+    }
   };
 
-  f32x16 o[VG::DG];
+  f32x16 o[DG];
 #pragma unroll
-  for (int dg = 0; dg < VG::DG; ++dg)
+  for (int dg = 0; dg < DG; ++dg)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dg][v] = 0.f;
   float m = kNegInf, l = 0.f;
 
   load(0);
-  store(0);
-  if (1 < ntiles) load(1);
   __syncthreads();
   // Tiles in three runs for this wave: keys every row of the wave sees, keys
   // near its rows (masked per lane: past the segment end or, causal, past
@@ -233,6 +190,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
       const char *b = buf(it);
       Chunk<DT> af[G::KCH];
       read_frag<DT, D>(af, b);
+      if (it + 1 < ntiles) load(it + 1);
       f32x16 s[1];
       tile_mma<DT, D, 1>(af, qf, s);
       // Raw logits; invisible keys (past the segment end, or later than the
@@ -256,7 +214,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
         const float alpha = fast_exp2(m - m_new);  // 0 while m is still -inf
         l *= alpha;
 #pragma unroll
-        for (int dg = 0; dg < VG::DG; ++dg)
+        for (int dg = 0; dg < DG; ++dg)
 #pragma unroll
           for (int v = 0; v < 16; ++v) o[dg][v] *= alpha;
         m = m_new;
@@ -268,14 +226,12 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
       const Chunk<DT> p0 = pack_p<DT>(p, 0), p1 = pack_p<DT>(p, 1);
       const char *vt = b + G::TILE;
 #pragma unroll
-      for (int dg = 0; dg < VG::DG; ++dg) {
-        o[dg] = mma<DT>(read_vt<DT, D>(vt, dg, 0), p0, o[dg]);
-        o[dg] = mma<DT>(read_vt<DT, D>(vt, dg, 1), p1, o[dg]);
+      for (int dg = 0; dg < DG; ++dg) {
+        o[dg] = mma<DT>(read_vt<DT, D>(vt, vt_off, dg, 0), p0, o[dg]);
+        o[dg] = mma<DT>(read_vt<DT, D>(vt, vt_off, dg, 1), p1, o[dg]);
       }
-    }
-    if (it + 1 < ntiles) {
-      store(it + 1);
-      if (it + 2 < ntiles) load(it + 2);
+    } else if (it + 1 < ntiles) {
+      load(it + 1);
     }
     __syncthreads();
   };
@@ -294,7 +250,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
     typedef typename PackT<DT>::T E;
     char *orow = reinterpret_cast<char *>(fa.out) + ((long long)t * fa.o_st + (long long)h * fa.o_sh) * G::ES;
 #pragma unroll
-    for (int dg = 0; dg < VG::DG; ++dg) {
+    for (int dg = 0; dg < DG; ++dg) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = dg * 32 + 8 * i + 4 * (lane >> 5);  // columns d .. d+3 in registers 4i .. 4i+3
