@@ -49,6 +49,19 @@ __device__ __forceinline__ Chunk<DT> pack_p(const float (&p)[16], int c) {
 // Column groups of O^T: 32 output columns each (the last one padded).
 template <int D> struct OGroups { static constexpr int DG = (D + 31) / 32; };
 
+// Row stride of the value tile, in 16-byte slots: the smallest that holds a
+// row and is 64 or 192 bytes past a multiple of 256.  A transposing read
+// touches four consecutive rows per 32 lanes, 64 bytes of each; with that
+// stride they start 16 banks apart (of 64) and never share a bank.  It also
+// leaves room for the padded columns of the last column group (d = 72, 80).
+constexpr int vt_slots(int units) {
+  int s = units;
+  while ((16 * s) % 256 != 64 && (16 * s) % 256 != 192) ++s;
+  return s;
+}
+template <int DT, int D>
+using VGeom = Geom<DT, D, vt_slots(Geom<DT, D>::UNITS)>;
+
 // This lane's byte offset into a row-major value tile for the transposing
 // reads.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group
 // receives value i % 4 of the 8-byte units that lanes i/4 + 4m (m = 0..3) of
@@ -60,18 +73,18 @@ template <int D> struct OGroups { static constexpr int DG = (D + 31) / 32; };
 // further on.
 template <int DT, int D>
 __device__ __forceinline__ int vt_lane_offset() {
-  using G = Geom<DT, D>;
+  using G = VGeom<DT, D>;
   const int lane = lane_id(), gr = lane >> 4, j = lane & 15;
   return (4 * (gr >> 1) + (j >> 2)) * G::RS + (16 * (gr & 1) + 4 * (j & 3)) * G::ES;
 }
 
 // V^T fragment of column group dg, key chunk c: lane column dg*32 + lane%32,
 // keys 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (h = lane / 32).  Columns
-// from D on read padding or the next row and only reach O^T rows that are
+// from D on read the row's zero padding and only reach O^T rows that are
 // never written out.
 template <int DT, int D>
 __device__ __forceinline__ Chunk<DT> read_vt(const char *vtile, int lane_off, int dg, int c) {
-  using G = Geom<DT, D>;
+  using G = VGeom<DT, D>;
   typedef short s4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4 lds_s4;
   const char *p = vtile + lane_off + 16 * c * G::RS + dg * 32 * G::ES;
@@ -87,7 +100,9 @@ template <int DT, int D>
 __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   using G = Geom<DT, D>;
   constexpr int DG = OGroups<D>::DG;
-  constexpr int BUF = 2 * G::TILE;  // key tile, then value tile
+  using VG = VGeom<DT, D>;
+  static_assert(OGroups<D>::DG * 32 * G::ES <= VG::RS, "padded columns stay inside a value row");
+  constexpr int BUF = G::TILE + VG::TILE;  // key tile, then value tile
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
   const AttnArgs &a = fa.at;
 
@@ -139,7 +154,8 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   const long long krow = a.k_st * G::ES;
   const char *vbase = reinterpret_cast<const char *>(fa.v) + (long long)g * fa.v_sh * G::ES;
   const long long vrow = fa.v_st * G::ES;
-  StageDirect<DT, D> sk, sv;
+  StageDirect<DT, D> sk;
+  StageDirect<DT, D, VG> sv;
   sk.init([&](int r) { return r * (int)krow; });
   sv.init([&](int r) { return r * (int)vrow; });
   const int vt_off = vt_lane_offset<DT, D>();

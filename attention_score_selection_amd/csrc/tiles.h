@@ -107,20 +107,25 @@ constexpr int kch(int dt, int d) {
 // multiple of the k width (72 for 16-bit types) is padded with zeros to the
 // next one: the padded units are staged as zeros and the padded k values of
 // the resident operand are zero, so they add nothing to the contraction.
-template <int DT, int D>
+// SLOTS (0: one more than the row's units) sets the LDS row stride in 16-byte
+// slots.
+template <int DT, int D, int SLOTS = 0>
 struct Geom {
   static_assert((D * Elem<DT>::ES) % 16 == 0, "a row must be whole 16-byte units");
   static constexpr int ES = Elem<DT>::ES;
   static constexpr int KW = Elem<DT>::KW;
   static constexpr int KCH = kch(DT, D);               // KW-wide k chunks (one MFMA step each)
   static constexpr int ROW = KCH * KW * ES;            // bytes of a (padded) row in LDS
-  static constexpr int RS = ROW + 16;                  // LDS row stride (bank spread)
   static constexpr int UNITS = ROW / 16;               // 16-byte units per (padded) row
   static constexpr int UNITS_D = D * ES / 16;          // ... of which hold data
   static constexpr int UPT = (kRows * UNITS + 255) / 256;  // units per thread (256 threads)
-  // LDS tile: 16-byte slots, UNITS + 1 per row (the last pads the row), the
-  // slot count rounded up to whole 64-slot blocks (one wave's direct load).
-  static constexpr int SLOTS_ROW = UNITS + 1;
+  // LDS tile: 16-byte slots, SLOTS_ROW per row (by default UNITS + 1, the
+  // last padding the row so that the 32 rows of a fragment read fall in
+  // different banks), the slot count rounded up to whole 64-slot blocks (one
+  // wave's direct load).
+  static_assert(SLOTS == 0 || SLOTS >= UNITS, "a row needs its units");
+  static constexpr int SLOTS_ROW = SLOTS ? SLOTS : UNITS + 1;
+  static constexpr int RS = 16 * SLOTS_ROW;            // LDS row stride in bytes
   static constexpr int NBLK = (kRows * SLOTS_ROW + 63) / 64;
   static constexpr int TILE = NBLK * 64 * 16;          // bytes of one tile
 };
@@ -196,9 +201,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // round-robin; each lane's slot maps to a fixed (row, 16-byte unit), whose
 // byte offset from the tile base is computed once.  Padding slots, and rows
 // past the valid range, read as zero.
-template <int DT, int D>
+template <int DT, int D, typename GT = Geom<DT, D>>
 struct StageDirect {
-  using G = Geom<DT, D>;
+  using G = GT;
   static constexpr int BPW = (G::NBLK + 3) / 4;  // blocks per wave (at most)
   int off[BPW];  // byte offset of this lane's unit in block 4*j + wave
   int row[BPW];  // its tile row (kRows: padding or past the tile)
