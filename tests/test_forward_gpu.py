@@ -98,6 +98,28 @@ def test_forward_lse_matches_oracle_and_identity_values(dev):
     assert np.nanmax(np.abs(lse - ref_lse)) <= 1e-4
 
 
+@pytest.mark.parametrize("mask,dtype,d", [("causal", "bf16", 80), ("blockdiag", "f16", 128)])
+def test_forward_fused_qkv_projection(dev, mask, dtype, d):
+    """Q, K and V as views into one fused [T, Hq + 2*Hkv, d] projection, so
+    the key and value tiles are copied from rows (Hq + 2*Hkv)*d elements
+    apart; d = 80 also has a padded last column group."""
+    hq, hkv = 8, 2
+    prob = random_medium(463 + d, mask, dtype=dtype, hq=hq, hkv=hkv, d=d, n_req=2)
+    announce(prob, "fused qkv")
+    qkv = torch.empty((prob.T, hq + 2 * hkv, d), dtype=prob.q.dtype)
+    qkv[:, :hq] = prob.q
+    qkv[:, hq:hq + hkv] = prob.k
+    qkv[:, hq + hkv:] = prob.v
+    g = qkv.to(dev)
+    q, k, v = g[:, :hq], g[:, hq:hq + hkv], g[:, hq + hkv:]
+    lay = tsel.Layout.from_problem(prob, dev)
+    scale = prob.softmax_scale if prob.softmax_scale is not None else 0.0
+    out, lse = tsel.tsel_attention_fwd(q, k, v, lay, prob.mask, scale)
+    torch.cuda.synchronize(dev)
+    ref_o, ref_lse = oracle.attention_forward(prob, workers=oracle.default_workers())
+    check(prob, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_o, ref_lse)
+
+
 def test_forward_empty_and_imageless_requests(dev):
     reqs = [(0, []), (37, [(5, 4, 6)]), (0, []), (20, []), (41, [(0, 3, 3), (12, 5, 5)])]
     prob = make_problem("fwd_empties", reqs, 4, 2, 64, "bf16", "causal", 1.0, 461,
