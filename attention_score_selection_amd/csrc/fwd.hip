@@ -21,7 +21,7 @@
 // The running maximum only moves when a tile's maximum exceeds it by more
 // than 2^8 (so P stays below 2^8, safe for f16 operands); the accumulators are
 // rescaled then, and the LSE uses the final maximum and sum.
-#include "tiles.h"
+#include "vtile.h"
 
 namespace tsel {
 
@@ -46,38 +46,6 @@ __device__ __forceinline__ Chunk<DT> pack_p(const float (&p)[16], int c) {
   return r;
 }
 
-// Column groups of O^T: 32 output columns each (the last one padded).
-template <int D> struct OGroups { static constexpr int DG = (D + 31) / 32; };
-
-// Row stride of the value tile, in 16-byte slots: the smallest that holds a
-// row and is 64 or 192 bytes past a multiple of 256.  A transposing read
-// touches four consecutive rows per 32 lanes, 64 bytes of each; with that
-// stride they start 16 banks apart (of 64) and never share a bank.  It also
-// leaves room for the padded columns of the last column group (d = 72, 80).
-constexpr int vt_slots(int units) {
-  int s = units;
-  while ((16 * s) % 256 != 64 && (16 * s) % 256 != 192) ++s;
-  return s;
-}
-template <int DT, int D>
-using VGeom = Geom<DT, D, vt_slots(Geom<DT, D>::UNITS)>;
-
-// This lane's byte offset into a row-major value tile for the transposing
-// reads.  ds_read_b64_tr_b16 works on groups of 16 lanes: lane i of a group
-// receives value i % 4 of the 8-byte units that lanes i/4 + 4m (m = 0..3) of
-// its group address.  Here lane j of group gr = lane/16 addresses the four
-// values of columns 16*(gr % 2) + 4*(j % 4) .. +3 in key row 4*(gr / 2) + j/4,
-// so lane i receives, for its own column 16*(gr % 2) + i = lane % 32, the
-// values of keys 4*(gr / 2) + 0..3 = 4*(lane / 32) + 0..3: the first four k
-// slots of its lane half.  The next four (keys + 8) are the same read 8 rows
-// further on.
-template <int DT, int D>
-__device__ __forceinline__ int vt_lane_offset() {
-  using G = VGeom<DT, D>;
-  const int lane = lane_id(), gr = lane >> 4, j = lane & 15;
-  return (4 * (gr >> 1) + (j >> 2)) * G::RS + (16 * (gr & 1) + 4 * (j & 3)) * G::ES;
-}
-
 // V^T fragment of column group dg, key chunk c: lane column dg*32 + lane%32,
 // keys 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3} (h = lane / 32).  Columns
 // from D on read the row's zero padding and only reach O^T rows that are
@@ -87,6 +55,7 @@ __device__ __forceinline__ Chunk<DT> read_vt(const char *vtile, int lane_off, in
   using G = VGeom<DT, D>;
   typedef short s4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s4 lds_s4;
+  // vtile + vt_read_offset(lane, dg, c, 0 / 1), the lane part held in lane_off.
   const char *p = vtile + lane_off + 16 * c * G::RS + dg * 32 * G::ES;
   const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)p);
   const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4 *)(p + 8 * G::RS));
@@ -158,7 +127,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   StageDirect<DT, D, VG> sv;
   sk.init([&](int r) { return r * (int)krow; });
   sv.init([&](int r) { return r * (int)vrow; });
-  const int vt_off = vt_lane_offset<DT, D>();
+  const int vt_off = vt_lane_offset_of<DT, D>(lane_id());
   auto buf = [&](int it) { return smem + (it & 1) * BUF; };
   // Start copying key and value tile it into its buffer (one scalar base per
   // tile; rows past key_hi read as zero).
