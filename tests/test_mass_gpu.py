@@ -107,9 +107,11 @@ def test_budget_mass_empty_and_zero_pools(dev):
     assert k[1] == oracle.budget_k(0.25, 24)  # zero mass: the lower bound
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_budget_mass_on_column_scores(dev, cfg):
-    """The GPU column score of a named workload, handed unchanged to both sides."""
+    """The GPU column score of a named workload (one pool of 3072, 30720 or
+    15000 candidates, or the varlen batch's eight pools), handed unchanged to
+    both sides."""
     prob = make_config(cfg)
     announce(prob.name)
     lay = tsel.Layout.from_problem(prob, dev)
