@@ -130,10 +130,12 @@ def test_forward_empty_and_imageless_requests(dev):
     check(prob, out, lse, ref_o, ref_lse)
 
 
-def test_forward_decoder_16384_sampled_rows(dev):
-    """The 16384-token GQA decoder layer at full size: 24 sampled rows of
-    every head against the row-at-a-time oracle."""
-    prob = make_config(4)
+@pytest.mark.parametrize("cfg", [4, 5, 3])
+def test_forward_named_workload_sampled_rows(dev, cfg):
+    """A named workload at full size (the 16384-token GQA decoder layer, the
+    varlen batch in f16, the 30-image block-diagonal workload at d = 80): 24
+    sampled rows of every head against the row-at-a-time oracle."""
+    prob = make_config(cfg)
     announce(prob)
     out, lse = run_fwd(prob, dev)
     rows = np.linspace(0, prob.T - 1, 24).astype(int)
