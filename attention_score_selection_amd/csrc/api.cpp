@@ -414,18 +414,25 @@ static void job_weights(const tsel_attn_t *a, const tsel_layout_t *l, const Attn
 // Heaviest-first job order for launches over several segments (varlen
 // batches): jobs are enumerated segment by segment, so without it the light
 // jobs of one request run before the heavy jobs of the next and the tail of
-// the launch grows.  Left in enumeration order when the weights already do
-// not increase (one causal segment, equal segments) or there are too many
-// jobs per head block for the permutation to travel in the arguments.  The
-// column score runs an XCD's jobs rank by rank across its head blocks, the LSE
-// head block by head block.  The forward keeps enumeration order: its jobs
-// also stream V, and mixing requests within an XCD costs it more L2 reuse than
-// the order wins (measured on an 8-request varlen batch).
+// the launch grows.  The column score of one causal segment is reordered too:
+// its row chunks are enumerated first to last, each with its key blocks in
+// order, so the half-visible diagonal jobs and the empty ones (a chunk before
+// the block) are spread through the launch; heaviest first (empty jobs last),
+// the 16384-token GQA layer's column score measured 1.8% faster, 5% with fp8
+// inputs.  Left in enumeration order when the weights already do not increase
+// (one causal segment of row blocks, equal segments) or there are too many
+// jobs per head block for the permutation to travel in the arguments (row-block
+// launches keep a limit of 512).  The column score runs an XCD's jobs rank by
+// rank across its head blocks, the LSE head block by head block.  The forward
+// keeps enumeration order: its jobs also stream V, and mixing requests within
+// an XCD costs it more L2 reuse than the order wins (measured on an 8-request
+// varlen batch).
 static void set_order(AttnArgs &x, JobPerm &perm, const tsel_attn_t *a, const tsel_layout_t *l,
                       const AttnPlan &p, bool keyblocks, int mode) {
   x.order = kOrderPlain;
   memset(perm.w, 0, sizeof(perm.w));
-  if (mode == kOrderPlain || p.nseg < 2 || p.jobs_per_hb > kOrderMaxJobs || p.KS > 0) return;
+  const long long cap = keyblocks ? kOrderMaxJobs : 512;
+  if (mode == kOrderPlain || (p.nseg < 2 && !keyblocks) || p.jobs_per_hb > cap || p.KS > 0) return;
   std::vector<int> w;
   job_weights(a, l, p, keyblocks, w);
   if ((long long)w.size() != p.jobs_per_hb) return;

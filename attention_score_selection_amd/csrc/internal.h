@@ -25,9 +25,10 @@ enum SegKind { SEG_REQ = 0, SEG_IMG = 1 };
 // permutation travels in the kernel arguments, so launches with at most
 // kOrderMaxJobs jobs per head block can be reordered.  Only the reordered
 // launches carry it: a kilobyte more of kernel arguments measured 6% slower
-// on the column score.
+// on the column score.  (The 16384-token GQA layer's column score has 570
+// jobs per head block.)
 enum JobOrder { kOrderPlain = 0, kOrderRankMajor = 1, kOrderSorted = 2 };
-constexpr int kOrderMaxJobs = 512;
+constexpr int kOrderMaxJobs = 1024;
 struct JobPerm {
   unsigned w[kOrderMaxJobs / 2];  // heaviest-first job permutation, 16 bits per entry (low half first)
 };
