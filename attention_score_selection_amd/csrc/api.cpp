@@ -225,7 +225,7 @@ int plan_lse(const tsel_attn_t *a, const tsel_layout_t *l, AttnPlan *p) {
     p->total_jobs = all;
     p->jobs_per_hb = all / p->nhb;
   };
-  const int ng_max = max_groups(dtype_of(a), a->head_dim);
+  const int ng_max = lse_groups(dtype_of(a), a->head_dim);
   long long all, real, nmax;
   count(ng_max, 0, all, real, nmax);
   if (all >= 512) {

@@ -633,7 +633,7 @@ __global__ __launch_bounds__(256) void colscore_finalize(AttnArgs a, float *scor
 namespace {
 
 template <int DT, int D>
-constexpr int kNGMax = max_groups(DT, D);
+constexpr int kNGMax = lse_groups(DT, D);
 template <int DT, int D>
 constexpr int kColNG = colscore_groups(DT, D);
 

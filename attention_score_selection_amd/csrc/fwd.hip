@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   using VG = VGeom<DT, D>;
   static_assert(OGroups<D>::DG * 32 * G::ES <= VG::RS, "padded columns stay inside a value row");
   constexpr int BUF = G::TILE + VG::TILE;  // key tile, then value tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) char stage0[BUF];
+  __shared__ __attribute__((aligned(16))) char stage1[BUF];
   const AttnArgs &a = fa.at;
 
   const int job = xcd_job(blockIdx.x, gridDim.x);
@@ -128,21 +129,18 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   sk.init([&](int r) { return r * (int)krow; });
   sv.init([&](int r) { return r * (int)vrow; });
   const int vt_off = vt_lane_offset_of<DT, D>(lane_id());
-  auto buf = [&](int it) { return smem + (it & 1) * BUF; };
-  // Start copying key and value tile it into its buffer (one scalar base per
-  // tile; rows past key_hi read as zero).
-  auto load = [&](int it) {
+  // Start copying key and value tile it into buffer dst (one scalar base per
+  // tile).  Rows past key_hi read as zero: the last tile's resources end
+  // after its valid rows (a valid row's units lie below nv row strides, every
+  // later row's at or above), so no per-lane row test is needed.
+  auto load = [&](int it, char *dst) {
     const long long first = key_lo + kRows * it;
     const int nv = key_hi - (int)first;
-    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kbase + first * krow);
-    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vbase + first * vrow);
-    if (nv >= kRows) {
-      sk.template load_at<false>(buf(it), krs, 0, kRows);
-      sv.template load_at<false>(buf(it) + G::TILE, vrs, 0, kRows);
-    } else {
-      sk.template load_at<true>(buf(it), krs, 0, nv);
-      sv.template load_at<true>(buf(it) + G::TILE, vrs, 0, nv);
-    }
+    const bool whole = nv >= kRows;
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kbase + first * krow, whole ? kOOB : nv * (int)krow);
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vbase + first * vrow, whole ? kOOB : nv * (int)vrow);
+    sk.template load_at<false>(dst, krs, 0, kRows);
+    sv.template load_at<false>(dst + G::TILE, vrs, 0, kRows);
   };
 
   f32x16 o[DG];
@@ -152,7 +150,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
     for (int v = 0; v < 16; ++v) o[dg][v] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  load(0);
+  load(0, stage0);
   __syncthreads();
   // Tiles in three runs for this wave: keys every row of the wave sees, keys
   // near its rows (masked per lane: past the segment end or, causal, past
@@ -168,14 +166,19 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
   const int full_end = uni(tiles_upto(a.causal ? min(key_hi - 1, wtok0) : key_hi - 1));
   const int seen_end = uni(a.causal ? tiles_from(wtok_max) : ntiles);
 
-  auto step = [&](int it, auto mode) {
+  // Tile it sits in stage it % 2, named at compile time (ST) so that the
+  // compiler sees the reads of this tile and the copy into the other stage
+  // touch different LDS objects and does not make the reads wait for it.
+  auto step = [&](int it, auto mode, auto st) {
     constexpr int MODE = decltype(mode)::value;  // 0: skipped, 1: masked, 2: every key visible
+    constexpr int ST = decltype(st)::value;
+    char *const b = ST ? stage1 : stage0;
+    char *const nb = ST ? stage0 : stage1;
     if (MODE != 0) {
       const int k0 = key_lo + kRows * it;
-      const char *b = buf(it);
       Chunk<DT> af[G::KCH];
       read_frag<DT, D>(af, b);
-      if (it + 1 < ntiles) load(it + 1);
+      if (it + 1 < ntiles) load(it + 1, nb);
       f32x16 s[1];
       tile_mma<DT, D, 1>(af, qf, s);
       // Raw logits; invisible keys (past the segment end, or later than the
@@ -216,14 +219,24 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel(FwdArgs fa) {
         o[dg] = mma<DT>(read_vt<DT, D>(vt, vt_off, dg, 1), p1, o[dg]);
       }
     } else if (it + 1 < ntiles) {
-      load(it + 1);
+      load(it + 1, nb);
     }
     __syncthreads();
   };
   int it = 0;
-  for (; it < full_end; ++it) step(it, std::integral_constant<int, 2>{});
-  for (; it < seen_end; ++it) step(it, std::integral_constant<int, 1>{});
-  for (; it < ntiles; ++it) step(it, std::integral_constant<int, 0>{});
+  const std::integral_constant<int, 0> s0;
+  const std::integral_constant<int, 1> s1;
+  auto run = [&](int end, auto mode) {
+    if ((it & 1) && it < end) step(it++, mode, s1);
+    for (; it + 1 < end; it += 2) {
+      step(it, mode, s0);
+      step(it + 1, mode, s1);
+    }
+    if (it < end) step(it++, mode, s0);
+  };
+  run(full_end, std::integral_constant<int, 2>{});
+  run(seen_end, std::integral_constant<int, 1>{});
+  run(ntiles, std::integral_constant<int, 0>{});
 
   // Both lane halves hold the same rows over different keys: combine the sums.
   const float lt = l + __shfl_xor(l, 32, 64);

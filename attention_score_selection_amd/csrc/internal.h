@@ -227,4 +227,12 @@ constexpr int colscore_groups(int dtype, int head_dim) {
 }
 constexpr int colscore_wgs(int dtype) { return dtype == TSEL_FP8_E4M3 ? 3 : 2; }
 
+// Resident query groups per wave of the LSE kernel.  A lane's 16 values of a
+// group all belong to one query row, so the row's offset and sum are one
+// register each and a fourth group fits where max_groups allows three
+// (16-bit inputs, d = 96..128).
+constexpr int lse_groups(int dtype, int head_dim) {
+  return max_groups(dtype, head_dim) == 3 && dtype != TSEL_F32 ? 4 : max_groups(dtype, head_dim);
+}
+
 }  // namespace tsel

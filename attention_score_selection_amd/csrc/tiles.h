@@ -137,12 +137,13 @@ constexpr int kOOB = kBufferLimit;
 // Buffer resource for raw (unstructured) loads from `base`; on gfx9 parts the
 // third word selects 32-bit data format so that offset range checking applies.
 // `base` must be wave-uniform; it is moved to scalar registers explicitly so
-// that the resource never needs a per-lane loop.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base) {
+// that the resource never needs a per-lane loop.  Loads at byte offsets from
+// `limit` on (wave-uniform, at most kOOB) return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int limit = kOOB) {
   const unsigned long long p = reinterpret_cast<unsigned long long>(base);
   const unsigned long long u = (unsigned long long)(unsigned)uni((int)(p >> 32)) << 32 |
                                (unsigned)uni((int)(unsigned)p);
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), (short)0, kOOB, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), (short)0, uni(limit), 0x00020000);
 }
 
 // Register staging of one streamed tile: global -> VGPR -> LDS.  Each thread
