@@ -784,6 +784,11 @@ int tsel_attention_fwd(const tsel_attn_t *attn, const tsel_layout_t *layout, con
     return fail(TSEL_EINVAL, "out strides must be positive and multiples of 8 bytes");
   if (32LL * v_stride_tok * es >= kBufferLimit)
     return fail(TSEL_EUNSUPPORTED, "strides too large: a 32-row tile spans 2 GiB or more");
+  // The kernel zeroes the key and value rows past a tile's valid range by
+  // ending that tile's buffer range after its last valid row, which needs
+  // rows that do not overlap in memory.
+  if (attn->k_stride_tok < attn->head_dim || v_stride_tok < attn->head_dim)
+    return fail(TSEL_EUNSUPPORTED, "the attention forward needs k and v token strides of at least head_dim");
   AttnPlan p;
   if ((rc = plan_fwd(attn, layout, &p)) != TSEL_OK) return rc;
   FwdArgs x{};

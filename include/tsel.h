@@ -243,7 +243,9 @@ int tsel_compact(const tsel_layout_t *layout, const uint8_t *keep, const void *e
  * over the row's visible keys (the masks and segments of tsel_lse), and
  * lse[h, i] exactly as tsel_lse computes it.  bf16 or f16 inputs only
  * (TSEL_EUNSUPPORTED otherwise); v is [T, Hkv, head_dim] in the same type,
- * 16-byte aligned, strides (elements) multiples of 16 bytes; out is
+ * 16-byte aligned, strides (elements) multiples of 16 bytes; the token strides
+ * of k and v must be at least head_dim (rows that do not overlap in memory;
+ * TSEL_EUNSUPPORTED otherwise); out is
  * [T, Hq, head_dim] in the same type, 8-byte aligned, strides multiples of
  * 8 bytes; lse fp32 [Hq, T].  No workspace. */
 int tsel_attention_fwd(const tsel_attn_t *attn, const tsel_layout_t *layout, const void *v,

@@ -286,6 +286,13 @@ def test_attention_fwd_validation(lib):
         B.TSEL_EINVAL
     assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 250, 128, FAKE, 1024, 128, FAKE, None) == B.TSEL_EINVAL
     assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 256, 128, FAKE, 1023, 128, FAKE, None) == B.TSEL_EINVAL
+    # Token strides below head_dim (rows overlapping in memory) are refused for k and for v.
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 64, 128, FAKE, 1024, 128, FAKE, None) == \
+        B.TSEL_EUNSUPPORTED
+    assert "token strides" in last_error(lib)
+    a.k_stride_tok = 64
+    assert f(ctypes.byref(a), ctypes.byref(lay.c), FAKE, 256, 128, FAKE, 1024, 128, FAKE, None) == \
+        B.TSEL_EUNSUPPORTED
 
 
 def test_mrope_validation(lib):
