@@ -120,6 +120,26 @@ def test_forward_fused_qkv_projection(dev, mask, dtype, d):
     check(prob, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_o, ref_lse)
 
 
+@pytest.mark.parametrize("mask,dtype,hq,hkv,d", [("causal", "bf16", 8, 2, 128), ("full", "f16", 4, 4, 80),
+                                                 ("blockdiag", "bf16", 6, 3, 72)])
+def test_forward_head_major_kv(dev, mask, dtype, hq, hkv, d):
+    """K and V stored head-major ([Hkv, T, d]) and passed as [T, Hkv, d] views:
+    the token stride is exactly head_dim, so a key or value row ends where the
+    next begins, and a ragged last tile's valid rows reach the very end of the
+    range its copy may read."""
+    prob = random_medium(471 + d, mask, dtype=dtype, hq=hq, hkv=hkv, d=d, n_req=2)
+    announce(prob, "head-major k/v")
+    k = prob.k.permute(1, 0, 2).contiguous().to(dev).permute(1, 0, 2)
+    v = prob.v.permute(1, 0, 2).contiguous().to(dev).permute(1, 0, 2)
+    assert k.stride(0) == d and v.stride(0) == d
+    lay = tsel.Layout.from_problem(prob, dev)
+    scale = prob.softmax_scale if prob.softmax_scale is not None else 0.0
+    out, lse = tsel.tsel_attention_fwd(prob.q.to(dev), k, v, lay, prob.mask, scale)
+    torch.cuda.synchronize(dev)
+    ref_o, ref_lse = oracle.attention_forward(prob, workers=oracle.default_workers())
+    check(prob, out.cpu().double().numpy(), lse.cpu().double().numpy(), ref_o, ref_lse)
+
+
 def test_forward_empty_and_imageless_requests(dev):
     reqs = [(0, []), (37, [(5, 4, 6)]), (0, []), (20, []), (41, [(0, 3, 3), (12, 5, 5)])]
     prob = make_problem("fwd_empties", reqs, 4, 2, 64, "bf16", "causal", 1.0, 461,
