@@ -3,12 +3,15 @@ issues for its own share of a tile and which complete only when that wave's
 vector-memory counter drains.  A tile is read by every wave of the workgroup,
 so each wave must wait for its copies before the barrier that precedes the
 reads: a barrier reached while a copy may still be in flight lets another wave
-read a half-written tile.  The kernels leave that wait to the compiler (the
-workgroup fence of __syncthreads() drains the counter; the reads of the other
-stage are not made to wait).  This test compiles the kernel sources for gfx950
-with the library's flags and checks the emitted code: along every control-flow
-path of every kernel, no s_barrier is reached after an LDS-direct load without
-an s_waitcnt vmcnt(0) in between.  Planted snippets pin the checker itself.
+read a half-written tile.  Likewise every LDS read of a stage must have
+returned before the barrier after which a copy into that stage may start.  The
+kernels leave both waits to the compiler (the workgroup fence of
+__syncthreads() drains both counters; the reads of one stage are not made to
+wait for a copy into the other).  This test compiles the kernel sources for
+gfx950 with the library's flags and checks the emitted code: along every
+control-flow path of every kernel, no s_barrier is reached after an LDS-direct
+load without an s_waitcnt vmcnt(0) in between, nor after an LDS read without an
+s_waitcnt lgkmcnt(0) in between.  Planted snippets pin the checker itself.
 CPU only (cross-compiles; nothing runs on a GPU)."""
 import os
 import re
@@ -76,21 +79,25 @@ def _blocks(body):
     return blocks, succ
 
 
-def _step(ins, pending, found=None):
+LDS_COPY = (r"^buffer_load_\w+\s.*\blds\b", "vmcnt(0)")   # LDS-direct load, drained by vmcnt(0)
+LDS_READ = (r"^ds_(read|load)", "lgkmcnt(0)")                # LDS read, drained by lgkmcnt(0)
+
+
+def _step(ins, pending, kind, found=None):
     for t in ins:
-        if re.match(r"^buffer_load_\w+\s.*\blds\b", t):
+        if re.match(kind[0], t):
             pending = True
-        elif t.startswith("s_waitcnt") and "vmcnt(0)" in t:
+        elif t.startswith("s_waitcnt") and kind[1] in t:
             pending = False
         elif t.startswith("s_barrier") and pending and found is not None:
             found.append(t)
     return pending
 
 
-def unsafe_barriers(asm_text):
-    """(kernel, barriers, LDS-direct loads, barriers reachable with a load in
-    flight) per kernel of an assembly listing: a forward may-analysis, the
-    in-flight flag joined by OR where paths meet."""
+def unsafe_barriers(asm_text, kind=LDS_COPY):
+    """(kernel, barriers, LDS-direct loads, barriers reachable with an access
+    of `kind` in flight) per kernel of an assembly listing: a forward
+    may-analysis, the in-flight flag joined by OR where paths meet."""
     out = []
     for name, body in _functions(asm_text.splitlines()):
         blocks, succ = _blocks(body)
@@ -99,13 +106,13 @@ def unsafe_barriers(asm_text):
         while changed:
             changed = False
             for i, b in enumerate(blocks):
-                if _step(b["ins"], state_in[i]):
+                if _step(b["ins"], state_in[i], kind):
                     for j in succ[i]:
                         if not state_in[j]:
                             state_in[j] = changed = True
         bad = []
         for i, b in enumerate(blocks):
-            _step(b["ins"], state_in[i], bad)
+            _step(b["ins"], state_in[i], kind, bad)
         nbar = sum(t.startswith("s_barrier") for b in blocks for t in b["ins"])
         ndma = sum(bool(re.match(r"^buffer_load_\w+\s.*\blds\b", t)) for b in blocks for t in b["ins"])
         out.append((name, nbar, ndma, len(bad)))
@@ -148,6 +155,9 @@ def test_checker_catches_planted_races():
     assert unsafe_barriers(PLANTED_BAD)[0][3] == 1
     assert unsafe_barriers(PLANTED_LOOP)[0][3] == 1
     assert unsafe_barriers(PLANTED_GOOD)[0][3] == 0
+    read = "_Zread:\n\tds_read_b128 v[0:3], v4\n\ts_waitcnt vmcnt(0)\n\ts_barrier\n\ts_endpgm\n.Lfunc_end3:\n"
+    assert unsafe_barriers(read, LDS_READ)[0][3] == 1
+    assert unsafe_barriers(read.replace("vmcnt(0)", "lgkmcnt(0)"), LDS_READ)[0][3] == 0
 
 
 @pytest.mark.parametrize("src", ["attn.hip", "fwd.hip"])
@@ -164,3 +174,5 @@ def test_no_barrier_with_lds_copy_in_flight(tmp_path, src):
           f"{sum(x[1] for x in streamed)} barriers, {sum(x[2] for x in streamed)} loads")
     bad = [(n[:80], k) for n, _, _, k in res if k]
     assert not bad, f"barriers reachable with an LDS-direct load in flight: {bad}"
+    bad = [(n[:80], k) for n, _, _, k in unsafe_barriers(asm.read_text(), LDS_READ) if k]
+    assert not bad, f"barriers reachable with an LDS read in flight: {bad}"
